@@ -1,0 +1,49 @@
+"""Plain, slow CPU oracle for the block-scaled FP8 linear layer.
+
+THIS PACKAGE IS TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it. The GPU library never
+calls it, and it shares no code with the HIP path: it has its own E4M3 table,
+its own bf16 rounding, its own dequant, quantizer and matmul, all written from
+the definitions on the pages.
+
+Sources (page titles and sections, not line numbers):
+
+* FastVideo PR #1829, "[feat] MiniMax H3: block-FP8 text encoder on Hopper, its
+  converter, and a 4xH100 FastH3 profile":
+    - "Purpose": each linear dequantizes its block-scaled weight to BF16 right
+      before a plain matmul.
+    - "Changes", converter bullet: E4M3 weight plus a [N/128, K/128]
+      ``weight_scale_inv`` grid.
+    - "Changes", tests bullet: the dequantizer is bit-exact against the
+      reference broadcast, and the FP8 round trip stays within E4M3 precision.
+* LightX2V PR #1657, "Walkthrough": FP8 GEMM with FP32 accumulation.
+* FastVideo ``fasth3_omniref_b200`` README, "What --lossless-accel turns on":
+  bf16 rounding happens at the same points as the eager ops.
+
+Every function is pinned by a ``-m "not gpu"`` test against something other
+than itself (closed forms, exact rational arithmetic, exhaustive enumeration,
+library routines on the host); see ``tests/test_oracle.py``. The only result
+left without such a pin is end-to-end model quality, which no page measures.
+"""
+
+from .fp8_block_ref import (  # noqa: F401
+    BLOCK,
+    E4M3_MAX,
+    BF16_CANONICAL_NAN,
+    e4m3_value,
+    e4m3_table,
+    bf16_bits_to_f32,
+    bf16_rne_bits,
+    bf16_rne_bits_nearest,
+    scale_grid_shape,
+    dequant,
+    dequant_rows,
+    e4m3_encode_nearest,
+    e4m3_encode_bits,
+    quantize,
+    linear_exact,
+    linear_sampled,
+    gemm_bound_ratio,
+    linear_bf16,
+    swiglu_bf16,
+)

@@ -1,0 +1,459 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something
+other than itself (closed forms, exact rational arithmetic, exhaustive or
+structured enumeration, hand-worked values, host library routines). Some
+tests plant a mistake in a copy of an oracle step to show the pin catches it.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import generate, random_problem
+
+
+def f32_from_bits(b):
+    return np.array([b], dtype=np.uint32).view(np.float32)[0]
+
+
+# ---------------------------------------------------------------------------
+# E4M3 decode table
+# ---------------------------------------------------------------------------
+
+def test_e4m3_closed_form_facts():
+    t = O.e4m3_table()
+    nan_codes = [c for c in range(256) if math.isnan(t[c])]
+    assert nan_codes == [0x7F, 0xFF]
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9           # subnormal step
+    assert t[0x08] == 2.0 ** -6           # smallest normal
+    assert t[0x07] == 7 * 2.0 ** -9       # largest subnormal
+    assert t[0x38] == 1.0
+    assert t[0x00] == 0.0 and not np.signbit(t[0x00])
+    assert t[0x80] == 0.0 and np.signbit(t[0x80])
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)       # strictly increasing over 0x00..0x7E
+    for c in range(0x7F):
+        assert t[c | 0x80] == -t[c]
+    finite = t[np.isfinite(t)]
+    assert finite.size == 254
+    assert np.unique(finite).size == 253  # +0 and -0 coincide
+
+
+def test_e4m3_enumeration_by_binade():
+    """Independent construction: 8 subnormals, 14 full binades of 8, and the
+    top binade with its last (NaN) slot removed: 127 non-negative codes."""
+    vals = [Fraction(m, 512) for m in range(8)]
+    for e in range(1, 16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append(Fraction(8 + m, 8) * Fraction(2) ** (e - 7))
+    assert len(vals) == 127
+    t = O.e4m3_table()
+    assert [Fraction(float(v)) for v in t[:0x7F]] == vals
+
+
+def test_e4m3_values_exact_in_bf16():
+    t = O.e4m3_table()
+    finite = t[np.isfinite(t)].astype(np.float32)
+    assert np.array_equal(O.bf16_bits_to_f32(O.bf16_rne_bits(finite)), finite)
+
+
+def test_e4m3_table_matches_torch_float8_e4m3fn():
+    torch = pytest.importorskip("torch")
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t = O.e4m3_table()
+    assert np.array_equal(np.isnan(ref), np.isnan(t))
+    fin = ~np.isnan(t)
+    assert np.array_equal(ref[fin], t[fin])
+    assert np.array_equal(np.signbit(ref[fin]), np.signbit(t[fin]))
+
+
+# ---------------------------------------------------------------------------
+# bf16 round to nearest even
+# ---------------------------------------------------------------------------
+
+def _structured_f32_patterns():
+    """Every (sign, exponent, top-7-mantissa) prefix with 16 chosen low
+    halves (exact zero, the tie, one either side of it, the extremes...)."""
+    highs = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x3FFF, 0x7FFE, 0x7FFF, 0x8000, 0x8001, 0x8002,
+                     0xBFFF, 0xFFFE, 0xFFFF, 0x1234, 0x4000, 0xC000, 0x00FF, 0xFF00],
+                    dtype=np.uint32)
+    return (highs[:, None] | lows[None, :]).ravel()
+
+
+def test_bf16_two_implementations_agree_structured():
+    pats = _structured_f32_patterns()
+    rng = np.random.default_rng(123)
+    pats = np.concatenate([pats, rng.integers(0, 1 << 32, size=4_000_000, dtype=np.uint32)])
+    x = pats.view(np.float32)
+    a = O.bf16_rne_bits(x)
+    b = O.bf16_rne_bits_nearest(x)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.skipif(os.environ.get("FP8BL_EXHAUSTIVE") != "1",
+                    reason="all 2^32 fp32 patterns; set FP8BL_EXHAUSTIVE=1 (minutes)")
+def test_bf16_two_implementations_agree_exhaustive():
+    step = 1 << 26
+    for start in range(0, 1 << 32, step):
+        pats = np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)
+        x = pats.view(np.float32)
+        assert np.array_equal(O.bf16_rne_bits(x), O.bf16_rne_bits_nearest(x)), hex(start)
+
+
+def test_bf16_spot_values():
+    cases = {
+        0x3F800000: 0x3F80,   # 1.0
+        0x3F808000: 0x3F80,   # tie, lower neighbour even
+        0x3F818000: 0x3F82,   # tie, upper neighbour even
+        0x3F808001: 0x3F81,   # just above the tie
+        0x3F807FFF: 0x3F80,   # just below the tie
+        0x80000000: 0x8000,   # -0
+        0x00000000: 0x0000,
+        0x7F7FFFFF: 0x7F80,   # largest fp32 rounds to +inf
+        0x7F7F7FFF: 0x7F7F,   # stays finite
+        0x7F7F8000: 0x7F80,   # tie at the top, odd lower -> inf
+        0xFF7F8000: 0xFF80,
+        0x00008000: 0x0000,   # subnormal tie to even (zero)
+        0x00018000: 0x0002,   # subnormal tie to even (2)
+        0x00010000: 0x0001,   # smallest bf16 subnormal
+        0x7F800000: 0x7F80,   # +inf
+        0xFF800000: 0xFF80,   # -inf
+        0x7FC00001: 0x7FC0,   # NaN -> canonical
+        0xFFFFFFFF: 0x7FC0,
+    }
+    x = np.array(list(cases.keys()), dtype=np.uint32).view(np.float32)
+    exp = np.array(list(cases.values()), dtype=np.uint16)
+    assert np.array_equal(O.bf16_rne_bits(x), exp)
+    assert np.array_equal(O.bf16_rne_bits_nearest(x), exp)
+
+
+def test_bf16_matches_torch_cast_on_finite():
+    torch = pytest.importorskip("torch")
+    pats = _structured_f32_patterns()
+    x = pats.view(np.float32)
+    keep = ~np.isnan(x)
+    x = x[keep]
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_rne_bits(x), ref)
+
+
+# ---------------------------------------------------------------------------
+# Dequant
+# ---------------------------------------------------------------------------
+
+def _exact_dequant_one(code, scale32):
+    """R(fl32(e4m3(code) * s)): the fp64 product of a 4-bit and a 24-bit
+    significand is exact (or an exact overflow/underflow-free value), then one
+    rounding to fp32 and the second bf16 implementation."""
+    v = O.e4m3_value(code)
+    s = float(scale32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.float32(v * s)
+    return int(O.bf16_rne_bits_nearest(np.array([p], dtype=np.float32))[0])
+
+
+def _scale_set():
+    rng = np.random.default_rng(7)
+    s = [1.0, 0.5, 2.0, 3.0, 1.0 / 448, 0.02 / 448, 1e-3, 7.5e-5]
+    s += [2.0 ** e for e in range(-30, 31, 3)]
+    s += list(rng.uniform(1e-6, 1e-2, size=40))
+    s += list(rng.standard_normal(10) * 1e-3)            # negative scales too
+    s += [2.0 ** -127, 2.0 ** -140, 2.0 ** -149, 1e-39]  # subnormal scales
+    s += [2.0 ** 120, 3.0e38]                            # overflow for big codes
+    s += [f32_from_bits(0x3FEB8E39), f32_from_bits(0x3DCCCCCD)]
+    s += [math.inf, 0.0, -0.0, math.nan]
+    return np.array(s, dtype=np.float32)
+
+
+def test_dequant_exhaustive_codes_times_scales():
+    scales = _scale_set()
+    codes = np.arange(256, dtype=np.uint8)
+    for s in scales:
+        q = codes.reshape(1, 256)
+        got = O.dequant(q, np.full((1, 2), s, dtype=np.float32))[0]
+        exp = np.array([_exact_dequant_one(c, s) for c in range(256)], dtype=np.uint16)
+        assert np.array_equal(got, exp), (float(s), np.nonzero(got != exp))
+
+
+def test_dequant_golden_worked_examples(golden_dir):
+    path = os.path.join(golden_dir, "dequant_worked_examples.txt")
+    n = 0
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code, sbits, want = (int(t, 16) for t in line.split()[:3])
+        got = O.dequant(np.array([[code]], dtype=np.uint8),
+                        np.array([[f32_from_bits(sbits)]], dtype=np.float32))
+        assert int(got[0, 0]) == want, (hex(code), hex(sbits), hex(int(got[0, 0])), hex(want))
+        n += 1
+    assert n >= 10
+
+
+def test_dequant_power_of_two_scales_are_exact_and_follow_blocks():
+    """A ragged grid where each block has its own power-of-two scale: every
+    element must equal e4m3(code) * 2^j exactly, with j taken from the block
+    (n//128, k//128). A transposed or shifted grid fails this."""
+    n, k = 300, 272                       # 3x3 grid, partial last row and column block
+    gn, gk = O.scale_grid_shape(n, k)
+    assert (gn, gk) == (3, 3)
+    exps = np.arange(gn * gk).reshape(gn, gk) - 4
+    s = (2.0 ** exps).astype(np.float32)
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x11          # no NaN codes here
+    got = O.bf16_bits_to_f32(O.dequant(q, s)).astype(np.float64)
+    t = O.e4m3_table()
+    for i in range(n):
+        for j in range(0, k, 17):
+            assert got[i, j] == t[q[i, j]] * 2.0 ** exps[i // 128, j // 128]
+
+
+def test_dequant_matches_torch_reference_broadcast():
+    """The "reference broadcast" read literally: decode with the library's
+    float8_e4m3fn, expand the scale grid, multiply in fp32, cast to bf16."""
+    torch = pytest.importorskip("torch")
+    wl = generate("tiny")
+    lin = wl.linears[0]
+    q, s = O.quantize(lin.w)
+    qt = torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+    st = torch.from_numpy(s).repeat_interleave(128, 0).repeat_interleave(128, 1)[: q.shape[0], : q.shape[1]]
+    ref = (qt * st).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.dequant(q, s), ref)
+    # ragged shape with random codes and random scales
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 256, size=(200, 144), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0
+    s = rng.uniform(1e-5, 1e-1, size=(2, 2)).astype(np.float32)
+    qt = torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+    st = torch.from_numpy(s).repeat_interleave(128, 0).repeat_interleave(128, 1)[:200, :144]
+    ref = (qt * st).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.dequant(q, s), ref)
+
+
+def test_planted_single_rounding_is_caught():
+    """Plant a mistake in a copy of the dequant step: round the exact product
+    straight to bf16 (one rounding instead of fp32 then bf16). The exhaustive
+    scale set must contain cases where the two differ."""
+    mismatches = 0
+    for s in _scale_set():
+        if not np.isfinite(s) or s == 0:
+            continue
+        for c in range(256):
+            if c & 0x7F == 0x7F:
+                continue
+            p = O.e4m3_value(c) * float(s)
+            if p == 0 or not (2.0 ** -120 < abs(p) < 3.0e38):
+                continue
+            if _round_f64_to_bf16(p) != _exact_dequant_one(c, s):
+                mismatches += 1
+    assert mismatches > 0
+
+
+def _round_f64_to_bf16(p):
+    """Direct RNE of an fp64 value to bf16 (single rounding), by brute force
+    over the two bf16 neighbours with exact rationals."""
+    if p == 0:
+        return 0x8000 if math.copysign(1, p) < 0 else 0
+    f = Fraction(p)
+    sgn = 0x8000 if p < 0 else 0
+    a = abs(f)
+    # find the bf16 pattern below a
+    bits = int(np.array([abs(p)], dtype=np.float32).view(np.uint32)[0]) >> 16
+    for b in (bits - 1, bits, bits + 1):
+        lo = Fraction(float(O.bf16_bits_to_f32(np.array([b], dtype=np.uint16))[0]))
+        hi = Fraction(float(O.bf16_bits_to_f32(np.array([b + 1], dtype=np.uint16))[0]))
+        if lo <= a < hi:
+            if a - lo < hi - a or (a - lo == hi - a and b % 2 == 0):
+                return sgn | b
+            return sgn | (b + 1)
+    raise AssertionError("neighbour search failed")
+
+
+# ---------------------------------------------------------------------------
+# Quantize
+# ---------------------------------------------------------------------------
+
+def _encode_probe_values():
+    t = O.e4m3_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2                       # 5 significant bits: exact in fp32
+    pts = np.concatenate([t, mids, [448.0, 456.0, 464.0, 470.0, 480.0]]).astype(np.float32)
+    bits = pts.view(np.uint32).astype(np.int64)
+    offs = np.arange(-40, 41)
+    near = (bits[:, None] + offs[None, :]).ravel()
+    near = near[(near >= 0) & (near <= 0x43F00000)].astype(np.uint32)
+    rng = np.random.default_rng(5)
+    rnd = rng.integers(0, 0x43F00001, size=3_000_000, dtype=np.uint32)
+    sub = np.arange(0, 1 << 20, dtype=np.uint32)      # fp32 subnormals and tiny normals
+    v = np.concatenate([near, rnd, sub]).view(np.float32)
+    return np.concatenate([v, -v])
+
+
+def test_encoders_agree():
+    v = _encode_probe_values()
+    assert np.array_equal(O.e4m3_encode_nearest(v), O.e4m3_encode_bits(v))
+
+
+def test_encoder_matches_torch_cast_in_range():
+    torch = pytest.importorskip("torch")
+    v = _encode_probe_values()
+    v = v[np.abs(v) <= 448.0]
+    ref = torch.from_numpy(v.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode_nearest(v), ref)
+
+
+def test_encoder_saturates_and_keeps_sign():
+    v = np.array([448.0, 449.0, 464.0, 465.0, 1e6, -1e30, -0.0, 0.0, -1e-30, 1e-30,
+                  2.0 ** -10, 2.0 ** -10 + 2.0 ** -30, 3 * 2.0 ** -10], dtype=np.float32)
+    got = O.e4m3_encode_nearest(v)
+    assert list(got) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x80, 0x00,
+                         0x00, 0x01, 0x02]
+
+
+def test_quantize_scales_codes_and_round_trip():
+    wl = generate("tiny")
+    w = wl.linears[0].w
+    q, s = O.quantize(w)
+    assert s.shape == (3, 2)
+    t = O.e4m3_table()
+    assert not np.any((q & 0x7F) == 0x7F)             # never a NaN code
+    for i in range(3):
+        for j in range(2):
+            blk = w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128].astype(np.float64)
+            qb = q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                assert s[i, j] == 1.0 and np.all(qb == 0)
+                continue
+            # fl32(amax/448): fp64 quotient then fp32 is the correctly rounded
+            # fp32 quotient (53 >= 2*24 + 2)
+            assert s[i, j] == np.float32(amax / 448.0)
+            assert np.any((qb & 0x7F) == 0x7E)
+            recon = t[qb] * float(s[i, j])                 # exact in fp64
+            # E4M3's normal range starts at 2^-6; below it the step is 2^-9
+            normal = np.abs(blk) >= 2.0 ** -6 * float(s[i, j])
+            assert np.all(np.abs(recon - blk)[normal] <= 2.0 ** -4 * np.abs(blk)[normal])
+            assert np.all(np.abs(recon - blk)[~normal] <= 2.0 ** -10 * float(s[i, j]))
+    # the zero block and the saturating block of this workload
+    assert s[0, 0] == 1.0 and np.all(q[:128, :128] == 0)
+    sat = q[256:384, 128:256]
+    n_idx, k_idx = np.meshgrid(np.arange(256, 384), np.arange(128, 256), indexing="ij")
+    assert np.all((sat[((n_idx + k_idx) % 2) == 0] & 0x7F) == 0x7E)
+
+
+def test_quantize_ragged_grid_uses_present_elements_only():
+    _, w = random_problem(9, 1, 200, 160)
+    w[128:, :] *= 10.0                 # the partial last row block has its own amax
+    q, s = O.quantize(w)
+    assert s.shape == (2, 2)
+    for i, rs in enumerate([slice(0, 128), slice(128, 200)]):
+        for j, cs in enumerate([slice(0, 128), slice(128, 160)]):
+            assert s[i, j] == np.float32(float(np.max(np.abs(w[rs, cs]))) / 448.0)
+
+
+def test_full_round_trip_within_e4m3_precision():
+    """Quantize then dequantize: within 2^-4 + 2^-8 relative for normal codes
+    (the E4M3 step is bounded by 2^-4; the bf16 step adds at most 2^-8)."""
+    _, w = random_problem(21, 1, 384, 512)
+    q, s = O.quantize(w)
+    wd = O.bf16_bits_to_f32(O.dequant(q, s)).astype(np.float64)
+    s_full = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)[:384, :512]
+    normal = np.abs(w) >= 2.0 ** -6 * s_full
+    rel = np.abs(wd - w)[normal] / np.abs(w.astype(np.float64))[normal]
+    assert rel.max() <= 2.0 ** -4 + 2.0 ** -8
+
+
+# ---------------------------------------------------------------------------
+# Linear (fp64 matmul) and the bound
+# ---------------------------------------------------------------------------
+
+def _bf16_fraction(bits):
+    return Fraction(float(O.bf16_bits_to_f32(np.array([bits], dtype=np.uint16))[0]))
+
+
+@pytest.mark.parametrize("m,n,k", [(3, 5, 16), (8, 8, 32), (16, 12, 48)])
+def test_linear_exact_brute_force(m, n, k):
+    x, w = random_problem(m * 100 + n, m, n, k, w_std=0.5)
+    q, s = O.quantize(w)
+    wb = O.dequant(q, s)
+    y, a = O.linear_exact(x, wb)
+    u = 2.0 ** -53
+    for i in range(m):
+        for j in range(n):
+            ex = sum(_bf16_fraction(x[i, kk]) * _bf16_fraction(wb[j, kk]) for kk in range(k))
+            ab = sum(abs(_bf16_fraction(x[i, kk]) * _bf16_fraction(wb[j, kk])) for kk in range(k))
+            assert abs(Fraction(y[i, j]) - ex) <= k * u * ab
+            assert abs(Fraction(a[i, j]) - ab) <= k * u * ab
+
+
+def test_planted_transpose_is_caught():
+    """A copy of the linear step that forgets the transpose (X W instead of
+    X W^T, square shapes so it runs) must fail the brute-force comparison."""
+    x, w = random_problem(5, 16, 16, 16, w_std=0.5)
+    q, s = O.quantize(w)
+    wb = O.dequant(q, s)
+    xf = O.bf16_bits_to_f32(x).astype(np.float64)
+    wf = O.bf16_bits_to_f32(wb).astype(np.float64)
+    wrong = xf @ wf
+    exact = np.array([[float(sum(_bf16_fraction(x[i, kk]) * _bf16_fraction(wb[j, kk])
+                                 for kk in range(16))) for j in range(16)] for i in range(16)])
+    assert not np.allclose(wrong, exact)
+    y, _ = O.linear_exact(x, wb)
+    assert np.allclose(y, exact, rtol=0, atol=1e-12)
+
+
+def test_linear_sampled_agrees_with_full():
+    x, w = random_problem(8, 20, 300, 256)
+    q, s = O.quantize(w)
+    y, a = O.linear_exact(x, O.dequant(q, s))
+    rng = np.random.default_rng(0)
+    ms = rng.integers(0, 20, 50)
+    ns = rng.integers(0, 300, 50)
+    ys, as_ = O.linear_sampled(x, q, s, ms, ns)
+    assert np.allclose(ys, y[ms, ns], rtol=1e-13, atol=1e-13)
+    assert np.allclose(as_, a[ms, ns], rtol=1e-13, atol=1e-13)
+
+
+def test_bound_accepts_rounded_and_rejects_wrong():
+    x, w = random_problem(4, 32, 64, 256)
+    q, s = O.quantize(w)
+    y, a = O.linear_exact(x, O.dequant(q, s))
+    yb = O.linear_bf16(x, q, s)
+    assert O.gemm_bound_ratio(yb, y, a).max() <= 1.0
+    # a dropped k-block (the last 128 of K) must fail somewhere
+    y2, _ = O.linear_exact(x[:, :128], O.dequant(q, s)[:, :128])
+    bad = O.bf16_rne_bits(y2.astype(np.float32))
+    assert O.gemm_bound_ratio(bad, y, a).max() > 1.0
+    # sign flip fails
+    assert O.gemm_bound_ratio(bad ^ np.uint16(0x8000), y, a).max() > 1.0
+    # zero inputs: tolerance zero, only zero passes
+    z = np.zeros((2, 2))
+    assert O.gemm_bound_ratio(np.zeros((2, 2), np.uint16), z, z).max() == 0.0
+    assert O.gemm_bound_ratio(np.full((2, 2), 0x3F80, np.uint16), z, z).max() == np.inf
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU helper (input preparation for the MLP down projection)
+# ---------------------------------------------------------------------------
+
+def test_swiglu_against_torch_and_closed_form():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(2)
+    g = O.bf16_rne_bits(rng.standard_normal(20000).astype(np.float32) * 4)
+    u = O.bf16_rne_bits(rng.standard_normal(20000).astype(np.float32))
+    h = O.swiglu_bf16(g, u)
+    gt = torch.from_numpy(O.bf16_bits_to_f32(g).astype(np.float64))
+    silu = torch.nn.functional.silu(gt).to(torch.float32).to(torch.bfloat16)
+    ref = (silu * torch.from_numpy(O.bf16_bits_to_f32(u)).to(torch.bfloat16))
+    ref = ref.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(h, ref)
+    # silu(0) = 0
+    assert O.swiglu_bf16(np.array([0], np.uint16), np.array([0x3F80], np.uint16))[0] == 0
