@@ -1,0 +1,210 @@
+"""Benchmark of the block-scaled FP8 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fp8_block_linear call (fused dequant + GEMM, fp32 accumulation,
+bf16 output) over one batch of the workload's synthetic input, with X, Q, S
+already resident in HBM. Weights are drawn fp32 from the seeded generator and
+quantized on the GPU by fp8_block_quantize before timing. To keep the 256 MB
+Infinity Cache from serving the weights, the timed steps rotate over enough
+distinct (X, Q, S, Y) sets to exceed twice its size.
+
+Prints ONE JSON line: throughput over the K timed steps, the roofline of the
+dominant kernel (per-launch duration from HIP events recorded on the launch
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
+MALL_BYTES = 256 << 20
+
+# workload name -> (generator name, linear index, bound)
+WORKLOADS = {
+    "attn_proj": ("attn_proj", 0, "mfma"),
+    "mlp_gate": ("mlp_pair", 0, "mfma"),
+    "mlp_down": ("mlp_pair", 2, "mfma"),
+    "dit_qkv": ("dit_large_m", 0, "mfma"),
+    "dit_mlp_up": ("dit_large_m", 1, "mfma"),
+    "skinny_m16": ("skinny", 0, "hbm"),
+    "skinny_m1": ("skinny", 1, "hbm"),
+    "tiny": ("tiny", 0, "mfma"),
+}
+
+
+def alg_bytes(m, n, k):
+    gn, gk = -(-n // 128), -(-k // 128)
+    return 2 * m * k + n * k + 4 * gn * gk + 2 * m * n
+
+
+def cpu_baseline(lin, x_bits, budget_s=12.0):
+    """The oracle as it stands (dequant + fp64 matmul + bound inputs) on a
+    bounded row sample of the workload's X, on this host's cores."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, s = O.quantize(lin.w)
+    rows = 1
+    done_flops, done_t = 0.0, 0.0
+    while True:
+        xs = x_bits[:rows]
+        t0 = time.perf_counter()
+        wd = O.dequant(q, s)
+        O.linear_exact(xs, wd)
+        dt = time.perf_counter() - t0
+        done_flops, done_t = 2.0 * rows * lin.n * lin.k, dt
+        if dt * 2.5 > budget_s or rows >= x_bits.shape[0]:
+            break
+        rows = min(rows * 2, x_bits.shape[0])
+    return {
+        "value": done_flops / done_t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows} of {x_bits.shape[0]} rows of X against the full "
+                  f"{lin.n}x{lin.k} weight (dequant + fp64 Y* and sum|x w|), {done_t:.2f} s",
+        "seconds": done_t,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer would shard by rows of X, columns or rows of W; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_fp8_linear_amd as F
+    from workloads import generate
+
+    gen_name, idx, bound = WORKLOADS[args.workload]
+    wl = generate(gen_name)
+    lin = wl.linears[idx]
+    m, n, k = lin.m, lin.n, lin.k
+    x_bits = lin.x
+    if x_bits is None:                   # the MLP down input: any bf16 of that shape
+        from workloads import draw_x
+        x_bits = draw_x(np.random.default_rng(wl.seed + 100), m, k)
+
+    dev = torch.device("cuda:0")
+    if not F.device_supported(0):
+        raise RuntimeError("cuda:0 is not a gfx950 device")
+    set_bytes = 2 * m * k + n * k + 2 * m * n
+    rotate = args.rotate or int(min(64, max(1, -(-2 * MALL_BYTES // set_bytes))))
+
+    w_dev = torch.from_numpy(lin.w).to(dev)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    sets = []
+    for r in range(rotate):
+        q, s = F.fp8_block_quantize(w_dev)
+        x = x0.clone()
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        sets.append((x, q, s, y))
+    del w_dev
+    ws_bytes = F.workspace_size(m, n, k)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        x, q, s, y = sets[i % rotate]
+        F.fp8_block_linear(x, q, s, out=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_launch_s = float(np.mean(per_launch_ms)) / 1e3
+    med_launch_s = float(np.median(per_launch_ms)) / 1e3
+
+    flops = 2.0 * m * n * k
+    abytes = alg_bytes(m, n, k)
+    if bound == "hbm":
+        unit, value = "GB/s", abytes * args.steps / wall / 1e9
+        achieved, peak, r_unit = abytes / avg_launch_s / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        unit, value = "TFLOP/s", flops * args.steps / wall / 1e12
+        achieved, peak, r_unit = flops / avg_launch_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+
+    out = {
+        "metric": "FP8-block linear TFLOP/s (% bf16 MFMA peak) and weight GB/s (% HBM) at M<=32",
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "m": m, "n": n, "k": k,
+                   "weight": "e4m3 + fp32 128x128 scale_inv", "rotated_sets": rotate,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "bound": bound,
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": r_unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "median_launch_us": round(med_launch_s * 1e6, 3),
+            "alg_bytes": abytes,
+            "flops": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(lin, x_bits)
+        if bound == "hbm":
+            # oracle throughput expressed in the metric's unit (bytes of the sample)
+            rows = int(cb["sample"].split()[0])
+            cb["value"] = alg_bytes(rows, n, k) / cb.pop("seconds") / 1e9
+            cb["unit"] = "GB/s"
+        else:
+            cb.pop("seconds")
+        cb["value"] = round(cb["value"], 6)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,125 @@
+"""Block-scaled FP8 linear layer for MI355X (gfx950).
+
+Weights live as E4M3 bytes Q[N,K] plus one fp32 weight_scale_inv per
+128x128 block, S[ceil(N/128), ceil(K/128)] (FastVideo PR #1829, "[feat]
+MiniMax H3: block-FP8 text encoder on Hopper, its converter, and a 4xH100
+FastH3 profile", "Changes"). The library behind this module (libfp8bl.so,
+hand-written HIP) provides:
+
+* ``fp8_block_quantize(w)``  -> (q, s)     the converter's quantization
+* ``fp8_block_dequant(q, s)`` -> bf16 W_hat  bit-exact dequant
+* ``fp8_block_linear(x, q, s)`` -> bf16 Y = X W_hat^T, fp32 accumulation
+
+The functions here only marshal torch tensors (device memory and the current
+stream) into the C ABI declared in include/fp8bl.h; all arithmetic runs in
+the HIP kernels. There is no CPU fallback: without the built library every
+call raises.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    PATH_AUTO, PATH_SKINNY, PATH_TILED, Fp8blError, abi_version, device_supported,
+    status_string, workspace_size,
+)
+
+BLOCK = 128
+
+__all__ = [
+    "fp8_block_quantize", "fp8_block_dequant", "fp8_block_linear", "workspace_size",
+    "device_supported", "abi_version", "status_string", "Fp8blError",
+    "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "scale_grid_shape",
+]
+
+
+def scale_grid_shape(n: int, k: int) -> tuple[int, int]:
+    return ((n + BLOCK - 1) // BLOCK, (k + BLOCK - 1) // BLOCK)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.FP8BL_OK:
+        raise Fp8blError(status, where)
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fp8_block_quantize(w: torch.Tensor, q: torch.Tensor | None = None,
+                       s: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """fp32 w [N,K] -> (q uint8 [N,K], s fp32 [ceil(N/128), ceil(K/128)])."""
+    _need(w, torch.float32, "w")
+    n, k = w.shape
+    if q is None:
+        q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty(scale_grid_shape(n, k), dtype=torch.float32, device=w.device)
+    _need(q, torch.uint8, "q")
+    _need(s, torch.float32, "s")
+    if tuple(q.shape) != (n, k) or tuple(s.shape) != scale_grid_shape(n, k):
+        raise ValueError("output shapes do not match w")
+    with torch.cuda.device(w.device):
+        _check(_lib.quantize_raw(w.data_ptr(), q.data_ptr(), s.data_ptr(), n, k,
+                                 _stream(w.device)), "fp8_block_quantize")
+    return q, s
+
+
+def fp8_block_dequant(q: torch.Tensor, s: torch.Tensor,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """q uint8 [N,K] + s fp32 grid -> bf16 [N,K] (bit-exact)."""
+    _need(q, torch.uint8, "q")
+    _need(s, torch.float32, "s")
+    n, k = q.shape
+    if tuple(s.shape) != scale_grid_shape(n, k):
+        raise ValueError(f"scale grid must be {scale_grid_shape(n, k)}, got {tuple(s.shape)}")
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (n, k):
+        raise ValueError("out shape")
+    with torch.cuda.device(q.device):
+        _check(_lib.dequant_raw(q.data_ptr(), s.data_ptr(), out.data_ptr(), n, k,
+                                _stream(q.device)), "fp8_block_dequant")
+    return out
+
+
+def fp8_block_linear(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     path: int = PATH_AUTO) -> torch.Tensor:
+    """bf16 x [M,K], q uint8 [N,K], s fp32 grid -> bf16 y [M,N] = x W_hat^T."""
+    _need(x, torch.bfloat16, "x")
+    _need(q, torch.uint8, "q")
+    _need(s, torch.float32, "s")
+    m, k = x.shape
+    n, kq = q.shape
+    if kq != k:
+        raise ValueError(f"K mismatch: x has {k}, q has {kq}")
+    if tuple(s.shape) != scale_grid_shape(n, k):
+        raise ValueError(f"scale grid must be {scale_grid_shape(n, k)}, got {tuple(s.shape)}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out shape")
+    need = workspace_size(m, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(x.device):
+        _check(_lib.linear_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), out.data_ptr(),
+                               m, n, k, ws_ptr, ws_bytes, path, _stream(x.device)),
+               "fp8_block_linear")
+    return out

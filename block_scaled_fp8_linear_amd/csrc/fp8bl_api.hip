@@ -1,0 +1,177 @@
+// C ABI of the block-scaled FP8 linear library (declared in include/fp8bl.h).
+//
+// Host-side only: argument validation (done first, before any HIP call),
+// the gfx950 gate, path choice and workspace sizing. All device work is in
+// the kernel files; nothing here touches tensor data.
+#include "fp8bl.h"
+
+#include <atomic>
+#include <cstring>
+
+#include "fp8bl_internal.h"
+
+#define FP8BL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;     // every dimension fits int32
+constexpr int64_t kMaxElems = (int64_t)1 << 36;   // N*K and M*N (16-byte chunk index fits uint32)
+constexpr int kSkinnyMaxM = 32;
+
+// 0 = unknown, 1 = gfx950, 2 = other.
+std::atomic<int> g_arch[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t grid_elems(int64_t n, int64_t k) {
+  return (size_t)((n + FP8BL_BLOCK - 1) / FP8BL_BLOCK) * (size_t)((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK);
+}
+
+int check_nk(int64_t n, int64_t k) {
+  if (n < 0 || k <= 0 || (k % 16) != 0) return FP8BL_INVALID_ARG;
+  if (n >= kMaxDim || k >= kMaxDim || (n > 0 && n * k > kMaxElems)) return FP8BL_INVALID_ARG;
+  if ((n + FP8BL_BLOCK - 1) / FP8BL_BLOCK > 65535) return FP8BL_INVALID_ARG;
+  return FP8BL_OK;
+}
+
+// The current device must be a gfx950; the answer is cached per device.
+int gate_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8BL_HIP_ERROR;
+  if (dev < 0 || dev >= kMaxDevices) return FP8BL_UNSUPPORTED_DEVICE;
+  int state = g_arch[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BL_HIP_ERROR;
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? FP8BL_OK : FP8BL_UNSUPPORTED_DEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8BL_OK : FP8BL_HIP_ERROR; }
+
+int validate_linear(const uint16_t* x, const uint8_t* q, const float* s, const uint16_t* y,
+                    int64_t m, int64_t n, int64_t k, int path) {
+  if (path != FP8BL_PATH_AUTO && path != FP8BL_PATH_TILED && path != FP8BL_PATH_SKINNY)
+    return FP8BL_INVALID_ARG;
+  if (m < 0 || m >= kMaxDim) return FP8BL_INVALID_ARG;
+  int st = check_nk(n, k);
+  if (st != FP8BL_OK) return st;
+  if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && n > 0 && m * n > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  if (!x || !q || !s || !y) return FP8BL_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(s, 4))
+    return FP8BL_ALIGNMENT;
+  const size_t ybytes = (size_t)m * n * 2;
+  if (overlap(y, ybytes, x, (size_t)m * k * 2) || overlap(y, ybytes, q, (size_t)n * k) ||
+      overlap(y, ybytes, s, grid_elems(n, k) * 4))
+    return FP8BL_INVALID_ARG;
+  return FP8BL_OK;
+}
+
+}  // namespace
+
+FP8BL_EXPORT int fp8_block_abi_version(void) { return FP8BL_ABI_VERSION; }
+
+FP8BL_EXPORT const char* fp8_block_status_string(int status) {
+  switch (status) {
+    case FP8BL_OK: return "FP8BL_OK";
+    case FP8BL_INVALID_ARG: return "FP8BL_INVALID_ARG: null pointer, bad size, K % 16 != 0, bad path or overlapping output";
+    case FP8BL_ALIGNMENT: return "FP8BL_ALIGNMENT: data pointers must be 16-byte aligned (scales 4-byte)";
+    case FP8BL_WORKSPACE: return "FP8BL_WORKSPACE: workspace missing or smaller than fp8_block_linear_workspace_size";
+    case FP8BL_UNSUPPORTED_DEVICE: return "FP8BL_UNSUPPORTED_DEVICE: the current HIP device is not gfx950";
+    case FP8BL_HIP_ERROR: return "FP8BL_HIP_ERROR: a HIP runtime call failed";
+    default: return "FP8BL_UNKNOWN_STATUS";
+  }
+}
+
+FP8BL_EXPORT int fp8_block_device_supported(int device) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) return 0;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+FP8BL_EXPORT int fp8_block_dequant(const uint8_t* q, const float* scale_inv, uint16_t* w_bf16,
+                                   int64_t n, int64_t k, hipStream_t stream) {
+  int st = check_nk(n, k);
+  if (st != FP8BL_OK) return st;
+  if (n == 0) return FP8BL_OK;
+  if (!q || !scale_inv || !w_bf16) return FP8BL_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(w_bf16, 16) || !aligned(scale_inv, 4)) return FP8BL_ALIGNMENT;
+  const size_t wbytes = (size_t)n * k * 2;
+  if (overlap(w_bf16, wbytes, q, (size_t)n * k) ||
+      overlap(w_bf16, wbytes, scale_inv, grid_elems(n, k) * 4))
+    return FP8BL_INVALID_ARG;
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_dequant(q, scale_inv, w_bf16, n, k, stream));
+}
+
+FP8BL_EXPORT size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || (k % 16) != 0) return 0;
+  if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return 0;
+  const size_t a = fp8bl::tiled_workspace_bytes(m, n, k);
+  const size_t b = fp8bl::skinny_workspace_bytes(m, n, k);
+  return a > b ? a : b;
+}
+
+FP8BL_EXPORT int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_inv,
+                                     uint16_t* y, int64_t m, int64_t n, int64_t k,
+                                     void* workspace, size_t workspace_bytes, int path,
+                                     hipStream_t stream) {
+  int st = validate_linear(x, q, scale_inv, y, m, n, k, path);
+  if (st != FP8BL_OK) return st;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  const bool skinny = path == FP8BL_PATH_SKINNY || (path == FP8BL_PATH_AUTO && m <= kSkinnyMaxM);
+  const size_t need = skinny ? fp8bl::skinny_workspace_bytes(m, n, k)
+                             : fp8bl::tiled_workspace_bytes(m, n, k);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FP8BL_WORKSPACE;
+    if (!aligned(workspace, fp8bl::kWorkspaceAlign)) return FP8BL_ALIGNMENT;
+    if (overlap(workspace, need, y, (size_t)m * n * 2) ||
+        overlap(workspace, need, x, (size_t)m * k * 2) ||
+        overlap(workspace, need, q, (size_t)n * k) ||
+        overlap(workspace, need, scale_inv, grid_elems(n, k) * 4))
+      return FP8BL_INVALID_ARG;
+  }
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  const hipError_t e = skinny
+      ? fp8bl::launch_gemm_skinny(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream)
+      : fp8bl::launch_gemm_tiled(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream);
+  return hip_status(e);
+}
+
+FP8BL_EXPORT int fp8_block_linear(const uint16_t* x, const uint8_t* q, const float* scale_inv,
+                                  uint16_t* y, int64_t m, int64_t n, int64_t k,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fp8_block_linear_ex(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes,
+                             FP8BL_PATH_AUTO, stream);
+}
+
+FP8BL_EXPORT int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,
+                                    int64_t n, int64_t k, hipStream_t stream) {
+  int st = check_nk(n, k);
+  if (st != FP8BL_OK) return st;
+  if (n == 0) return FP8BL_OK;
+  if ((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK > 65535 * 4) return FP8BL_INVALID_ARG;
+  if (!w || !q || !scale_inv) return FP8BL_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale_inv, 4)) return FP8BL_ALIGNMENT;
+  const size_t sbytes = grid_elems(n, k) * 4;
+  if (overlap(q, (size_t)n * k, w, (size_t)n * k * 4) || overlap(scale_inv, sbytes, w, (size_t)n * k * 4) ||
+      overlap(q, (size_t)n * k, scale_inv, sbytes))
+    return FP8BL_INVALID_ARG;
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_quantize(w, q, scale_inv, n, k, stream));
+}

@@ -1,0 +1,64 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// the E4M3 -> fp32 -> bf16 dequant of packed codes, and small helpers.
+//
+// Dequant of one element (FastVideo PR #1829, "Purpose"):
+//   bf16_rne( fl32( e4m3(code) * scale ) )
+// The E4M3 decode uses the gfx950 hardware conversion (v_cvt_pk_f32_fp8,
+// OCP E4M3FN on this architecture: every finite code is exact in fp32), the
+// product is one IEEE fp32 multiply (no contraction: nothing is added to
+// it), and v_cvt_pk_bf16_f32 rounds two results to nearest-even at once.
+// fp32 denormals are kept (the library is built without flush-to-zero).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bl {
+
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr int kBlock = 128;  // scale-block edge
+
+// Two fp32 -> packed bf16 pair (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four E4M3 codes (byte i of `codes` is element i) -> two packed bf16 pairs,
+// each element scaled by `s` in fp32 first.
+__device__ __forceinline__ u32x2 dequant4(uint32_t codes, float s) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);  // bytes 0,1
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);   // bytes 2,3
+  u32x2 r;
+  r[0] = pack_bf16x2(__fmul_rn(lo[0], s), __fmul_rn(lo[1], s));
+  r[1] = pack_bf16x2(__fmul_rn(hi[0], s), __fmul_rn(hi[1], s));
+  return r;
+}
+
+// Eight codes (two dwords) -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t c0, uint32_t c1, float s) {
+  u32x2 a = dequant4(c0, s);
+  u32x2 b = dequant4(c1, s);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// bf16 NaN (exponent all ones, mantissa non-zero) -> the canonical 0x7FC0,
+// applied to both halves of a packed pair.
+__device__ __forceinline__ uint32_t canon_nan_bf16x2(uint32_t v) {
+  uint32_t lo = v & 0xFFFFu, hi = v >> 16;
+  lo = ((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo;
+  hi = ((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi;
+  return lo | (hi << 16);
+}
+
+}  // namespace fp8bl

@@ -1,0 +1,37 @@
+// Internal (non-exported) launchers behind the C ABI. Every launcher assumes
+// its arguments were validated by the ABI layer (sizes, alignment, K % 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8bl {
+
+hipError_t launch_dequant(const uint8_t* q, const float* s, uint16_t* w,
+                          int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_quantize(const float* w, uint8_t* q, float* s,
+                           int64_t n, int64_t k, hipStream_t stream);
+
+// Large-M fused GEMM (E4M3 tiles decoded to bf16 in registers, bf16 MFMA).
+size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s,
+                             uint16_t* y, int64_t m, int64_t n, int64_t k,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Skinny-M (M <= 32 rows per pass) weight-streaming GEMM.
+size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* s,
+                              uint16_t* y, int64_t m, int64_t n, int64_t k,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Deterministic sum of `splits` fp32 partial [M,N] slabs (in split order)
+// and one bf16 rounding into y.
+hipError_t launch_reduce_partials(const float* part, uint16_t* y, int splits,
+                                  int64_t m, int64_t n, hipStream_t stream);
+
+constexpr size_t kWorkspaceAlign = 256;
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace fp8bl

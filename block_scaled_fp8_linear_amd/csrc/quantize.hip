@@ -1,0 +1,103 @@
+// Block quantizer: fp32 W[N,K] -> E4M3 codes Q[N,K] + fp32 weight_scale_inv
+// S[GN,GK], the format the converter writes (FastVideo PR #1829, "Changes",
+// converter bullet: E4M3 weight plus [N/128, K/128] weight_scale_inv).
+//
+// Per 128x128 block (present elements only, for partial edge blocks):
+//   amax = max |w|;  S = fl32(amax / 448), or 1 when amax == 0;
+//   code = nearest finite E4M3 to fl32(w / S), ties to the even code,
+//          saturating at 448, sign kept.
+// One workgroup per block; offline work, so it favours exactness over speed
+// (two IEEE divisions per element).
+#include "fp8bl_device.h"
+#include "fp8bl_internal.h"
+
+namespace fp8bl {
+
+namespace {
+
+// Nearest E4M3FN code to a finite fp32 value (ties to even, saturating).
+// Normal range (|v| >= 2^-6): round the 23-bit fp32 mantissa to 3 bits by
+// adding half an E4M3 ulp minus one plus the kept lsb, then rebias the
+// exponent from 127 to 7 (the carry of a round-up walks into the exponent,
+// which is exactly the next code). Subnormal range: |v| * 2^9 is exact and
+// rintf rounds it to the nearest integer, ties to even; 8 becomes the
+// smallest normal code 0x08 by construction.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                 // |v| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {           // |v| < 2^-6
+    code = (uint32_t)rintf(__builtin_bit_cast(float, a) * 512.0f);
+  } else {
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads)
+void quantize_kernel(const float* __restrict__ w, uint8_t* __restrict__ q,
+                     float* __restrict__ s, int N, int K, int gk) {
+  __shared__ float wave_max[kThreads / 64];
+  const int bi = blockIdx.y, bj = blockIdx.x;
+  const int tid = threadIdx.x;
+  // Thread t covers row (t >> 1) of the block, columns (t & 1) * 64 .. +64.
+  const int row = bi * kBlock + (tid >> 1);
+  const int col0 = bj * kBlock + (tid & 1) * 64;
+  const bool row_ok = row < N;
+
+  f32x4 v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int col = col0 + c * 4;
+    if (row_ok && col < K) {
+      v[c] = *reinterpret_cast<const f32x4*>(w + (size_t)row * K + col);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])),
+                               fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
+    } else {
+      v[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+  if (tid == 0) s[bi * gk + bj] = sc;
+  if (!row_ok) return;
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const int col = col0 + c4 * 16;
+    if (col >= K) break;
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x4 t = v[c4 * 4 + d];
+      out[d] = e4m3_from_f32(__fdiv_rn(t[0], sc)) |
+               (e4m3_from_f32(__fdiv_rn(t[1], sc)) << 8) |
+               (e4m3_from_f32(__fdiv_rn(t[2], sc)) << 16) |
+               (e4m3_from_f32(__fdiv_rn(t[3], sc)) << 24);
+    }
+    *reinterpret_cast<u32x4*>(q + (size_t)row * K + col) = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* w, uint8_t* q, float* s, int64_t n, int64_t k,
+                           hipStream_t stream) {
+  const int gn = (int)((n + kBlock - 1) / kBlock);
+  const int gk = (int)((k + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(quantize_kernel, dim3((uint32_t)gk, (uint32_t)gn), dim3(kThreads), 0,
+                     stream, w, q, s, (int)n, (int)k, gk);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bl

@@ -1,0 +1,130 @@
+/*
+ * fp8bl.h — C ABI of the block-scaled FP8 linear library for MI355X (gfx950).
+ *
+ * Format (FastVideo PR #1829, "[feat] MiniMax H3: block-FP8 text encoder on
+ * Hopper, its converter, and a 4xH100 FastH3 profile", section "Changes",
+ * converter bullet): a weight W[N,K] (nn.Linear out x in) is held as
+ *   - Q[N,K]   one OCP E4M3FN byte per element, row-major, K contiguous;
+ *   - S[GN,GK] one fp32 weight_scale_inv per 128x128 block, row-major,
+ *              GN = ceil(N/128), GK = ceil(K/128); the last row/column block
+ *              may be partial.
+ * The block value is W ~ e4m3(Q) * S. Dequantization (same page, "Purpose")
+ * turns each element into bf16( fl32( e4m3(Q[n,k]) * S[n/128][k/128] ) ):
+ * an IEEE fp32 multiply, then round-to-nearest-even to bf16.
+ *
+ * Conventions shared by every call:
+ *   - All data pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller. The library never allocates, frees or synchronises; work
+ *     is enqueued on `stream` (NULL = the default stream) and the call returns.
+ *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *   - Row-major, contiguous. Dimensions are int64_t; zero rows or columns is a
+ *     no-op that returns FP8BL_OK. K must be a positive multiple of 16.
+ *   - Data pointers must be 16-byte aligned (scale grids 4-byte aligned,
+ *     workspaces 256-byte aligned). Outputs must not overlap inputs.
+ *   - Every argument error is reported by the return code BEFORE anything is
+ *     launched; no exception or abort crosses this interface. A fault inside a
+ *     kernel surfaces, as in HIP, at the caller's next synchronisation.
+ *   - The library keeps no state besides a per-device cached architecture
+ *     check; calls on different streams may run concurrently.
+ *   - Scales are expected finite; other scales still follow the dequant
+ *     formula (NaN products become the canonical bf16 NaN 0x7FC0).
+ */
+#ifndef FP8BL_H
+#define FP8BL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BL_ABI_VERSION 1
+#define FP8BL_BLOCK 128
+
+/* Return codes of every int-returning call. */
+enum fp8bl_status {
+  FP8BL_OK = 0,
+  FP8BL_INVALID_ARG = 1,        /* null pointer, negative or unsupported size, K % 16 != 0, overlap */
+  FP8BL_ALIGNMENT = 2,          /* a pointer is not aligned as required */
+  FP8BL_WORKSPACE = 3,          /* workspace missing or smaller than the queried size */
+  FP8BL_UNSUPPORTED_DEVICE = 4, /* the current device is not gfx950 */
+  FP8BL_HIP_ERROR = 5           /* a HIP runtime call failed (device query or launch) */
+};
+
+/* Kernel choice for fp8_block_linear_ex. AUTO picks SKINNY for M <= 32 and
+ * TILED otherwise; the other values force a path (for tests). */
+enum fp8bl_path {
+  FP8BL_PATH_AUTO = 0,
+  FP8BL_PATH_TILED = 1,
+  FP8BL_PATH_SKINNY = 2
+};
+
+/* Version of this interface (FP8BL_ABI_VERSION). */
+int fp8_block_abi_version(void);
+
+/* Static string naming a return code; never NULL. */
+const char* fp8_block_status_string(int status);
+
+/* The runtime gate (the page's validate_runtime / get_min_capability pair,
+ * FastVideo PR #1829 "Changes", first bullet): 1 if HIP device `device` is a
+ * gfx950, else 0 (also 0 when the device cannot be queried). Host only. */
+int fp8_block_device_supported(int device);
+
+/* Standalone dequant (FastVideo PR #1829, "Purpose": the block-scaled weight
+ * is dequantized to BF16 before a plain matmul; "Changes", tests bullet: the
+ * result is bit-exact against the reference broadcast).
+ *   q          [n,k] E4M3 bytes          (in, 16-B aligned)
+ *   scale_inv  [ceil(n/128),ceil(k/128)] fp32 (in, 4-B aligned)
+ *   w_bf16     [n,k] bf16 bits           (out, 16-B aligned, may not overlap)
+ * Output is bit-exact: bf16_rne(fl32(e4m3(q) * s)), NaN -> 0x7FC0. */
+int fp8_block_dequant(const uint8_t* q, const float* scale_inv, uint16_t* w_bf16,
+                      int64_t n, int64_t k, hipStream_t stream);
+
+/* Bytes of device workspace fp8_block_linear / fp8_block_linear_ex need for
+ * this shape with ANY path (0 when none). Host only; never fails. */
+size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_t k);
+
+/* The linear layer (FastVideo PR #1829, "Purpose": dequantize to BF16, then a
+ * plain matmul; LightX2V PR #1657, "Walkthrough": FP32 accumulation):
+ *   y[m,n] = bf16_rne( sum_k x[m,k] * What[n,k] ),  What as in fp8_block_dequant,
+ * with fp32 accumulation and one bf16 rounding per output. What is formed in
+ * registers only. No bias.
+ *   x          [m,k] bf16 bits  (in, 16-B aligned)
+ *   q, scale_inv                (in, as above)
+ *   y          [m,n] bf16 bits  (out, 16-B aligned, may not overlap)
+ *   workspace  device scratch of at least fp8_block_linear_workspace_size
+ *              bytes (256-B aligned), or NULL when that size is 0. Its contents
+ *              need no initialisation and are not preserved. Two calls that
+ *              share a workspace must be ordered (same stream). */
+int fp8_block_linear(const uint16_t* x, const uint8_t* q, const float* scale_inv,
+                     uint16_t* y, int64_t m, int64_t n, int64_t k,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fp8_block_linear with an explicit path (enum fp8bl_path). Same contract;
+ * any path accepts any shape. */
+int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_inv,
+                        uint16_t* y, int64_t m, int64_t n, int64_t k,
+                        void* workspace, size_t workspace_bytes, int path,
+                        hipStream_t stream);
+
+/* The converter's quantization (FastVideo PR #1829, "Changes", converter
+ * bullet: E4M3 weight plus per-128x128 weight_scale_inv). For each block:
+ *   amax = max |w| over the elements present in the block,
+ *   S    = fl32(amax / 448)  (IEEE division; 1.0 when amax == 0),
+ *   Q    = nearest finite E4M3 to fl32(w / S), ties to even code, saturating
+ *          at +-448, sign kept (-0 and negative underflow give 0x80).
+ *   w          [n,k] fp32, finite (in, 16-B aligned)
+ *   q          [n,k] E4M3 bytes (out, 16-B aligned)
+ *   scale_inv  [ceil(n/128),ceil(k/128)] fp32 (out, 4-B aligned)
+ * Bit-exact. Non-finite w gives unspecified codes and scales. */
+int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,
+                       int64_t n, int64_t k, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BL_H */

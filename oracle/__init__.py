@@ -42,6 +42,7 @@ from .fp8_block_ref import (  # noqa: F401
     e4m3_encode_bits,
     quantize,
     linear_exact,
+    linear_value,
     linear_sampled,
     gemm_bound_ratio,
     linear_bf16,

@@ -245,6 +245,13 @@ def linear_exact(x_bits: np.ndarray, w_bits: np.ndarray) -> tuple[np.ndarray, np
     return y, a
 
 
+def linear_value(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """Y* = X W_hat^T in fp64 alone (no A), for preparing derived inputs."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    return x @ w.T
+
+
 def linear_sampled(x_bits: np.ndarray, q: np.ndarray, scale_inv: np.ndarray,
                    ms: np.ndarray, ns: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Y*[ms[i], ns[i]] and A[ms[i], ns[i]] one output at a time (fp64), for

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, every
+function include/fp8bl.h declares is exported, and argument errors come back
+as status codes before anything touches a device."""
+
+import ctypes
+
+import pytest
+
+from block_scaled_fp8_linear_amd import _lib as L
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_header_symbols_exported(lib):
+    names = L.header_functions()
+    assert set(names) == {
+        "fp8_block_abi_version", "fp8_block_status_string", "fp8_block_device_supported",
+        "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
+        "fp8_block_linear_ex", "fp8_block_quantize",
+    }
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert L.abi_version() == 1
+    for st in range(6):
+        s = L.status_string(st)
+        assert s.startswith("FP8BL_")
+    assert L.status_string(99) == "FP8BL_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes():
+    assert L.workspace_size(0, 10, 16) == 0
+    assert L.workspace_size(4, 0, 16) == 0
+    assert L.workspace_size(4, 8, 15) == 0          # invalid K -> 0, never fails
+    for m, n, k in [(1, 8000, 8192), (16, 8000, 8192), (512, 5120, 5120), (64, 384, 256),
+                    (16384, 3072, 3072), (3, 100, 4096), (512, 5120, 25600)]:
+        ws = L.workspace_size(m, n, k)
+        assert ws % 256 == 0
+        assert ws <= 16 * m * n * 4 + 256
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced here
+
+
+@pytest.mark.parametrize("args,status", [
+    # (x, q, s, y, m, n, k, ws, ws_bytes, path)
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 8, 15, 0, 0, 0), L.FP8BL_INVALID_ARG),    # K % 16
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 8, 0, 0, 0, 0), L.FP8BL_INVALID_ARG),     # K == 0
+    ((FAKE, FAKE, FAKE, 4 * FAKE, -1, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),   # M < 0
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 4, -8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),   # N < 0
+    ((0, FAKE, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),       # null x
+    ((FAKE, 0, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),       # null q
+    ((FAKE, FAKE, 0, 4 * FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),       # null s
+    ((FAKE, FAKE, FAKE, 0, 4, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),           # null y
+    ((FAKE + 2, FAKE, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_ALIGNMENT),  # x misaligned
+    ((FAKE, FAKE + 8, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_ALIGNMENT),  # q misaligned
+    ((FAKE, FAKE, FAKE + 2, 4 * FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_ALIGNMENT),  # s misaligned
+    ((FAKE, FAKE, FAKE, 4 * FAKE + 4, 4, 8, 16, 0, 0, 0), L.FP8BL_ALIGNMENT),  # y misaligned
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),        # y overlaps x
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 7), L.FP8BL_INVALID_ARG),    # bad path
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 1 << 31, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),  # M too big
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 0, 8, 16, 0, 0, 0), L.FP8BL_OK),             # empty M: no-op
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 0, 16, 0, 0, 0), L.FP8BL_OK),             # empty N: no-op
+    ((0, 0, 0, 0, 0, 0, 16, 0, 0, 0), L.FP8BL_OK),                             # empty, null ok
+])
+def test_linear_argument_errors(lib, args, status):
+    x, q, s, y, m, n, k, ws, wsb, path = args
+    assert L.linear_raw(x, q, s, y, m, n, k, ws, wsb, path) == status
+
+
+def test_linear_workspace_errors(lib):
+    # a shape that needs a split-K workspace on the skinny path
+    m, n, k = 16, 64, 8192
+    need = L.workspace_size(m, n, k)
+    assert need > 0
+    x, q, s, y = FAKE, 8 * FAKE, 16 * FAKE, 24 * FAKE
+    assert L.linear_raw(x, q, s, y, m, n, k, 0, 0, L.PATH_SKINNY) == L.FP8BL_WORKSPACE
+    assert L.linear_raw(x, q, s, y, m, n, k, 32 * FAKE, 1024, L.PATH_SKINNY) == L.FP8BL_WORKSPACE
+    assert L.linear_raw(x, q, s, y, m, n, k, 32 * FAKE, 1024, L.PATH_TILED) == L.FP8BL_WORKSPACE
+    assert L.linear_raw(x, q, s, y, m, n, k, 32 * FAKE + 16, need, L.PATH_SKINNY) == L.FP8BL_ALIGNMENT
+    assert L.linear_raw(x, q, s, y, m, n, k, y, need, L.PATH_SKINNY) == L.FP8BL_INVALID_ARG
+
+
+def test_valid_call_without_gpu_reports_device_status(lib):
+    """With valid arguments the gate runs; on a machine without a gfx950 it
+    must answer with a status, not crash. (On the GPU machine this test is not
+    meaningful and is skipped.)"""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = L.linear_raw(FAKE, 8 * FAKE, 16 * FAKE, 24 * FAKE, 4, 8, 16, 0, 0, L.PATH_AUTO)
+    assert st in (L.FP8BL_HIP_ERROR, L.FP8BL_UNSUPPORTED_DEVICE)
+    assert L.device_supported(0) is False
+
+
+@pytest.mark.parametrize("n,k,qoff,soff,woff,status", [
+    (8, 15, 0, 0, 0, L.FP8BL_INVALID_ARG),
+    (-1, 16, 0, 0, 0, L.FP8BL_INVALID_ARG),
+    (8, 16, 8, 0, 0, L.FP8BL_ALIGNMENT),
+    (8, 16, 0, 2, 0, L.FP8BL_ALIGNMENT),
+    (8, 16, 0, 0, 4, L.FP8BL_ALIGNMENT),
+    (0, 16, 0, 0, 0, L.FP8BL_OK),
+])
+def test_dequant_and_quantize_argument_errors(lib, n, k, qoff, soff, woff, status):
+    q, s, w = FAKE + qoff, 8 * FAKE + soff, 16 * FAKE + woff
+    assert L.dequant_raw(q, s, w, n, k) == status
+    # quantize(w, q, s): w is the fp32 input
+    assert L.quantize_raw(w, q, s, n, k) == status
+    # overlapping output
+    assert L.dequant_raw(FAKE, 8 * FAKE, FAKE, 8, 16) == L.FP8BL_INVALID_ARG

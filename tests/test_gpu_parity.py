@@ -1,0 +1,308 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Dequant and quantize must match bit for bit; the linear must satisfy the
+bound |y - Y*| <= 2^-7 |Y*| + 1e-4 sum_k |x_k w_k| against the oracle's fp64
+Y*, plus exact invariants (one-hot identity, zero input, power-of-two
+scaling, run-to-run reproducibility). Inputs come from the seeded workload
+generators; weights are quantized by the oracle for every linear/dequant
+test, never by the GPU.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from workloads import generate, random_problem  # noqa: E402
+
+from gpu_util import bits, f32, say, to_bf16, to_f32, to_u8, u8  # noqa: E402
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+import block_scaled_fp8_linear_amd as F  # noqa: E402
+
+PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY}
+
+
+def run_linear(x_bits, q, s, path=F.PATH_AUTO):
+    xt, qt, st = to_bf16(x_bits), to_u8(q), to_f32(s)
+    y = F.fp8_block_linear(xt, qt, st, path=path)
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def assert_bound(y_bits, y_ref, a_ref, label):
+    ratio = O.gemm_bound_ratio(y_bits, y_ref, a_ref)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    say(label, "max bound ratio", worst)
+    assert worst <= 1.0, (label, worst, np.unravel_index(np.argmax(ratio), ratio.shape))
+
+
+# ---------------------------------------------------------------------------
+# device gate
+# ---------------------------------------------------------------------------
+
+def test_device_is_gfx950():
+    say("device", torch.cuda.get_device_name(0))
+    assert F.device_supported(0)
+
+
+# ---------------------------------------------------------------------------
+# dequant: bit-exact
+# ---------------------------------------------------------------------------
+
+def _scale_set():
+    rng = np.random.default_rng(7)
+    s = [1.0, 0.5, 2.0, 3.0, 1.0 / 448, 0.02 / 448, 1e-3, 7.5e-5]
+    s += [2.0 ** e for e in range(-30, 31, 3)]
+    s += list(rng.uniform(1e-6, 1e-2, size=40))
+    s += list(rng.standard_normal(10) * 1e-3)
+    s += [2.0 ** -127, 2.0 ** -140, 2.0 ** -149, 1e-39, 2.0 ** 120, 3.0e38]
+    s += [np.array([0x3FEB8E39], np.uint32).view(np.float32)[0]]
+    s += [np.inf, 0.0, -0.0, np.nan]
+    return np.array(s, dtype=np.float32)
+
+
+def test_dequant_all_codes_times_scales():
+    scales = _scale_set()
+    g = len(scales)
+    q = np.tile(np.arange(256, dtype=np.uint8), (128 * g, 1))          # [128g, 256]
+    s = np.repeat(scales[:, None], 2, axis=1).astype(np.float32)        # [g, 2]
+    say("dequant codes x scales", q.shape)
+    got = bits(F.fp8_block_dequant(to_u8(q), to_f32(s)))
+    exp = O.dequant(q, s)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+@pytest.mark.parametrize("n,k", [(1, 16), (300, 272), (129, 4096), (128, 128), (7, 2064)])
+def test_dequant_ragged_random(n, k):
+    rng = np.random.default_rng(n * 7 + k)
+    q = rng.integers(0, 256, size=(n, k), dtype=np.uint8)             # NaN codes included
+    s = rng.uniform(1e-5, 1e-1, size=O.scale_grid_shape(n, k)).astype(np.float32)
+    say("dequant ragged", n, k)
+    got = bits(F.fp8_block_dequant(to_u8(q), to_f32(s)))
+    assert np.array_equal(got, O.dequant(q, s))
+
+
+@pytest.mark.parametrize("name", ["tiny", "attn_proj", "skinny"])
+def test_dequant_workloads(name):
+    wl = generate(name)
+    lin = wl.linears[0]
+    q, s = O.quantize(lin.w)
+    say("dequant workload", name, q.shape)
+    got = bits(F.fp8_block_dequant(to_u8(q), to_f32(s)))
+    assert np.array_equal(got, O.dequant(q, s))
+
+
+# ---------------------------------------------------------------------------
+# quantize: bit-exact codes and scales
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "attn_proj", "skinny"])
+def test_quantize_workloads(name):
+    lin = generate(name).linears[0]
+    say("quantize workload", name, lin.w.shape)
+    qt, st = F.fp8_block_quantize(to_f32(lin.w))
+    torch.cuda.synchronize()
+    q, s = O.quantize(lin.w)
+    assert np.array_equal(f32(st).view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(u8(qt), q)
+
+
+@pytest.mark.parametrize("n,k,std", [(200, 160, 0.02), (1, 16, 1.0), (129, 272, 1e-30),
+                                     (300, 400, 1e3), (64, 1024, 0.02)])
+def test_quantize_ragged(n, k, std):
+    _, w = random_problem(n + k, 1, n, k, w_std=std)
+    w[: min(n, 5), :16] = 0.0
+    w[0, 0] = -0.0
+    if n > 128 and k > 128:
+        w[128:, 128:] = 0.0                                            # an all-zero block
+    say("quantize ragged", n, k, std)
+    qt, st = F.fp8_block_quantize(to_f32(w))
+    torch.cuda.synchronize()
+    q, s = O.quantize(w)
+    assert np.array_equal(f32(st).view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(u8(qt), q)
+
+
+def test_quantize_subnormal_and_tie_values():
+    """Values placed on E4M3 midpoints (ties) and deep in the subnormal
+    range of both formats, after the per-block scale is applied."""
+    t = O.e4m3_table()[:0x7F]
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    w = np.zeros((128, 256), dtype=np.float32)
+    w[0, :] = 448.0                                  # amax 448 -> S = 1 exactly
+    w[1:, :] = np.resize(np.concatenate([mids, -mids, t.astype(np.float32)]), (127, 256))
+    w[100:110, :] = np.float32(2.0 ** -140)          # fp32 subnormal inputs
+    say("quantize ties/subnormals")
+    qt, st = F.fp8_block_quantize(to_f32(w))
+    torch.cuda.synchronize()
+    q, s = O.quantize(w)
+    assert s[0, 0] == 1.0
+    assert np.array_equal(f32(st).view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(u8(qt), q)
+
+
+# ---------------------------------------------------------------------------
+# linear: bound against the fp64 oracle, both kernels forced on small shapes
+# ---------------------------------------------------------------------------
+
+SMALL_SHAPES = [
+    (64, 384, 256),      # the tiny workload's shape
+    (1, 384, 256),
+    (16, 200, 272),      # ragged N and K (K % 128 != 0)
+    (33, 300, 1040),     # just past the skinny threshold
+    (130, 513, 528),
+    (257, 640, 384),
+    (512, 256, 2048),
+    (5, 8, 16),          # smallest legal K
+]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_linear_small_shapes(m, n, k, path):
+    x, w = random_problem(m * 131 + n * 7 + k, m, n, k)
+    q, s = O.quantize(w)
+    say("linear", path, m, n, k)
+    y = run_linear(x, q, s, PATHS[path])
+    yr, ar = O.linear_exact(x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"{path} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_linear_tiny_workload(path):
+    lin = generate("tiny").linears[0]
+    q, s = O.quantize(lin.w)
+    say("linear tiny workload", path)
+    y = run_linear(lin.x, q, s, PATHS[path])
+    yr, ar = O.linear_exact(lin.x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"tiny {path}")
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_linear_one_hot_identity(path):
+    """X = I (M = K = 256): every output is a single exact product, so Y must
+    equal W_hat^T bit for bit: the GEMM consumes exactly the dequant's bf16."""
+    lin = generate("tiny").linears[0]
+    q, s = O.quantize(lin.w)
+    x = np.zeros((256, 256), dtype=np.uint16)
+    x[np.arange(256), np.arange(256)] = 0x3F80                    # bf16 1.0
+    say("one-hot identity", path)
+    y = run_linear(x, q, s, PATHS[path])
+    assert np.array_equal(y, O.dequant(q, s).T)
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_linear_zero_input_gives_positive_zero(path):
+    _, w = random_problem(3, 1, 300, 512)
+    q, s = O.quantize(w)
+    x = np.zeros((40, 512), dtype=np.uint16)
+    say("zero input", path)
+    y = run_linear(x, q, s, PATHS[path])
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_linear_power_of_two_scaling_is_exact(path):
+    x, w = random_problem(12, 48, 320, 768)
+    q, s = O.quantize(w)
+    x2 = O.bf16_rne_bits(O.bf16_bits_to_f32(x) * np.float32(4.0))   # exact
+    say("power-of-two scaling", path)
+    y1 = run_linear(x, q, s, PATHS[path])
+    y2 = run_linear(x2, q, s, PATHS[path])
+    assert np.array_equal(O.bf16_rne_bits(O.bf16_bits_to_f32(y1) * np.float32(4.0)), y2)
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_linear_reproducible(path):
+    x, w = random_problem(44, 24, 1000, 4096)
+    q, s = O.quantize(w)
+    say("reproducible", path)
+    xt, qt, st = to_bf16(x), to_u8(q), to_f32(s)
+    ys = [bits(F.fp8_block_linear(xt, qt, st, path=PATHS[path])) for _ in range(3)]
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+
+
+def test_linear_empty_shapes():
+    say("empty shapes")
+    q = to_u8(np.zeros((8, 32), np.uint8))
+    s = to_f32(np.ones((1, 1), np.float32))
+    y = F.fp8_block_linear(to_bf16(np.zeros((0, 32), np.uint16)), q, s)
+    assert tuple(y.shape) == (0, 8)
+    y = F.fp8_block_linear(to_bf16(np.zeros((4, 32), np.uint16)),
+                           to_u8(np.zeros((0, 32), np.uint8)), to_f32(np.ones((0, 1), np.float32)))
+    assert tuple(y.shape) == (4, 0)
+
+
+# ---------------------------------------------------------------------------
+# linear on the full workload sizes, in the launch configuration the
+# benchmark uses (AUTO path)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,idx", [("attn_proj", 0), ("skinny", 0), ("skinny", 1)])
+def test_linear_workload_full_compare(name, idx):
+    wl = generate(name)
+    lin = wl.linears[idx]
+    q, s = O.quantize(lin.w)
+    say("linear workload", name, lin.name, lin.m, lin.n, lin.k)
+    y = run_linear(lin.x, q, s)
+    yr, ar = O.linear_exact(lin.x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"{name}/{lin.name}")
+
+
+def _sample_idx(size, tile, rng, n_rand):
+    edges = {0, 1, size - 1, size - 2}
+    for b in range(tile, size, tile):
+        edges |= {b - 1, b}
+    edges = sorted(e for e in edges if 0 <= e < size)
+    if len(edges) > 24:
+        edges = list(rng.choice(edges, 24, replace=False))
+    return np.unique(np.concatenate([edges, rng.integers(0, size, n_rand)])).astype(np.int64)
+
+
+def _check_sampled(x_bits, q, s, y, label, n_rand=24):
+    m, n = y.shape
+    rng = np.random.default_rng(m + n)
+    ms = _sample_idx(m, 256, rng, n_rand)
+    ns = _sample_idx(n, 256, rng, n_rand)
+    mm, nn = np.meshgrid(ms, ns, indexing="ij")
+    mm, nn = mm.ravel(), nn.ravel()
+    yr, ar = O.linear_sampled(x_bits, q, s, mm, nn)
+    assert_bound(y[mm, nn], yr, ar, label + f" ({mm.size} sampled outputs)")
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_linear_dit_large_m_sampled(idx):
+    wl = generate("dit_large_m")
+    lin = wl.linears[idx]
+    q, s = O.quantize(lin.w)
+    say("linear workload dit_large_m", lin.name, lin.m, lin.n, lin.k)
+    y = run_linear(lin.x, q, s)
+    _check_sampled(lin.x, q, s, y, f"dit_large_m/{lin.name}")
+
+
+def test_linear_mlp_pair_sampled():
+    wl = generate("mlp_pair")
+    gate, up, down = wl.linears
+    qg, sg = O.quantize(gate.w)
+    qu, su = O.quantize(up.w)
+    qd, sd = O.quantize(down.w)
+    say("linear workload mlp_pair gate/up", gate.m, gate.n, gate.k)
+    yg = run_linear(gate.x, qg, sg)
+    _check_sampled(gate.x, qg, sg, yg, "mlp_pair/gate")
+    yu = run_linear(up.x, qu, su)
+    _check_sampled(up.x, qu, su, yu, "mlp_pair/up")
+    # The down input is the SwiGLU of the ORACLE's gate/up outputs.
+    g_ref = O.bf16_rne_bits(O.linear_value(gate.x, O.dequant(qg, sg)).astype(np.float32))
+    u_ref = O.bf16_rne_bits(O.linear_value(up.x, O.dequant(qu, su)).astype(np.float32))
+    h = O.swiglu_bf16(g_ref, u_ref)
+    say("linear workload mlp_pair down", down.m, down.n, down.k)
+    yd = run_linear(h, qd, sd)
+    _check_sampled(h, qd, sd, yd, "mlp_pair/down", n_rand=12)

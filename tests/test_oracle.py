@@ -417,6 +417,7 @@ def test_linear_sampled_agrees_with_full():
     rng = np.random.default_rng(0)
     ms = rng.integers(0, 20, 50)
     ns = rng.integers(0, 300, 50)
+    assert np.array_equal(O.linear_value(x, O.dequant(q, s)), y)
     ys, as_ = O.linear_sampled(x, q, s, ms, ns)
     assert np.allclose(ys, y[ms, ns], rtol=1e-13, atol=1e-13)
     assert np.allclose(as_, a[ms, ns], rtol=1e-13, atol=1e-13)
