@@ -98,7 +98,11 @@ def fp8_block_dequant(q: torch.Tensor, s: torch.Tensor,
 def fp8_block_linear(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                      path: int = PATH_AUTO) -> torch.Tensor:
-    """bf16 x [M,K], q uint8 [N,K], s fp32 grid -> bf16 y [M,N] = x W_hat^T."""
+    """bf16 x [M,K], q uint8 [N,K], s fp32 grid -> bf16 y [M,N] = x W_hat^T.
+
+    ``workspace``, when given, must hold at least ``workspace_size(M, N, K)``
+    bytes (fp32 split-K partials; no initialisation needed); calls sharing it
+    must be ordered."""
     _need(x, torch.bfloat16, "x")
     _need(q, torch.uint8, "q")
     _need(s, torch.float32, "s")

@@ -18,6 +18,8 @@ constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;     // every dimension fits int32
 constexpr int64_t kMaxElems = (int64_t)1 << 36;   // N*K and M*N (16-byte chunk index fits uint32)
 constexpr int kSkinnyMaxM = 32;
+// The GEMM kernels address a tile's rows with 32-bit buffer offsets.
+constexpr int64_t kMaxLinearK = (int64_t)1 << 20;
 
 // 0 = unknown, 1 = gfx950, 2 = other.
 std::atomic<int> g_arch[kMaxDevices];
@@ -64,6 +66,7 @@ int validate_linear(const uint16_t* x, const uint8_t* q, const float* s, const u
   if (m < 0 || m >= kMaxDim) return FP8BL_INVALID_ARG;
   int st = check_nk(n, k);
   if (st != FP8BL_OK) return st;
+  if (k > kMaxLinearK) return FP8BL_INVALID_ARG;
   if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
   if (m > 0 && n > 0 && m * n > kMaxElems) return FP8BL_INVALID_ARG;
   if (m == 0 || n == 0) return FP8BL_OK;

@@ -8,13 +8,23 @@
 // accumulators (LightX2V PR #1657, "Walkthrough": FP32 accumulation).
 //
 // Workgroup tile BM x BN, 4 waves side by side along N: wave w owns the
-// BN/4 weight rows [n0 + w*BN/4, ...) for all BM rows of X. So every weight
-// element is decoded exactly once per workgroup (decode cost per MFMA flop
-// falls as 1/BM), while the X tile is shared through LDS, staged with
-// 16-byte loads into an XOR-swizzled layout that the MFMA operand reads hit
-// without bank conflicts. A wave's rows lie inside one 128-row scale block
-// and a 64-wide K step inside one 128-column block, so each wave needs one
-// scalar scale per K step.
+// BN/4 weight rows [n0 + w*BN/4, ...) for all BM rows of X. Every weight
+// element is therefore decoded exactly once per workgroup (decode VALU per
+// MFMA flop falls as 1/BM), while the X tile is shared through LDS, staged
+// with 16-byte loads into an XOR-swizzled layout that the MFMA operand reads
+// hit without bank conflicts. A wave's rows lie inside one 128-row scale
+// block and a 64-wide K step inside one 128-column block, so each wave needs
+// one scalar scale per K step.
+//
+// Pipeline (one barrier per K step): a wave dequantizes the codes of step k
+// (loaded one step earlier), issues the loads of X and codes for step k+1,
+// runs step k's MFMAs from LDS and the decoded registers, then stages X for
+// step k+1 into the other LDS buffer. Two workgroups share each CU, so one
+// workgroup's decode overlaps the other's MFMAs. Loads go through buffer
+// descriptors covering only the tile's valid rows: rows past M or N and the
+// K tail read as zero without branches. (Measured alternatives that did not
+// pay on MI355X: decoding step k+1 inside step k's MFMA stream with two
+// operand sets, and prefetching two steps ahead.)
 //
 // MFMA v_mfma_f32_32x32x16_bf16 (gfx950): lane l supplies 8 consecutive-k
 // bf16 of row (l % 32) for A and of column (l % 32) for B; the two half-waves
@@ -23,8 +33,12 @@
 // 16-byte load of codes gives a lane the k chunks of two consecutive MFMAs;
 // the matching X chunks are read from LDS with the same permutation of k.
 //
-// Split-K (gridDim.y > 1) writes fp32 partials that a second kernel sums in
-// split order (deterministic) and rounds once to bf16.
+// Split-K (gridDim.y > 1): every split writes an fp32 partial tile to the
+// workspace and a second kernel adds the splits in split order
+// (deterministic) and rounds once to bf16. (Finishing the sum inside the
+// GEMM with a per-tile arrival counter needs a device-scope release/acquire
+// per workgroup, which on this multi-XCD part means an L2 write-back and
+// invalidate each time; measured about 3x slower than the second kernel.)
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
@@ -34,10 +48,27 @@ namespace {
 
 constexpr int kBK = 64;           // K per pipeline step
 constexpr int kThreads = 256;     // 4 waves
+constexpr uint32_t kOob = 0x80000000u;   // buffer offset past every valid range
 
 // XOR swizzle of 16-byte chunks inside a 128-byte LDS row (64 bf16 of K).
+// gfx950's LDS has 64 four-byte banks: two consecutive 128-byte rows fill
+// all of them, and a 16-byte read is served 16 lanes at a time. The MFMA
+// operand read has 16 lanes on 16 consecutive rows at one logical chunk;
+// XOR-ing the chunk with (row / 2) % 8 gives those lanes 16 distinct
+// 16-byte bank groups (row parity picks the half, the XOR the group), so
+// reads and the row-wise staging writes are conflict-free.
 __device__ __forceinline__ int xs_offset(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
+  return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword 3 = 0x00020000: raw (untyped) buffer, 32-bit data format, the
+  // layout gfx9-family descriptors use; out-of-range reads return zero.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 template <int BM, int BN, int MINB>
@@ -57,7 +88,7 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Tile order: consecutive workgroups are dealt round-robin to the 8 XCDs;
   // renumber so each XCD gets a contiguous run of tiles, then walk the run
@@ -80,48 +111,56 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   const int kt0 = blockIdx.y * kt_per_split;
   const int kt1 = min(kt0 + kt_per_split, nkt);
 
-  // ---- X staging: thread handles chunk (tid & 7) of rows (tid >> 3) + 32 i.
+  // ---- X: thread moves chunk (tid & 7) of tile rows (tid >> 3) + 32 i.
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(x + (size_t)m0 * K, (uint32_t)(min(M - m0, BM) * K * 2));
   const int xc = tid & 7;
   const int xr0 = tid >> 3;
+  const uint32_t xoff0 = (uint32_t)(xr0 * K * 2 + xc * 16);
+  const uint32_t xrow_stride = (uint32_t)(32 * K * 2);
+
+  // ---- W codes: lane holds 16 codes of row (lane % 32) of each column
+  // block, k chunk (lane / 32) of each 32-wide k slab.
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(q + (size_t)n0 * K, (uint32_t)(max(min(N - n0, BN), 0) * K));
+  const int wkoff = (lane >> 5) * 16;
+  const uint32_t woff0 = (uint32_t)((wave * WN + (lane & 31)) * K + wkoff);
+  const uint32_t wnb_stride = (uint32_t)(32 * K);
+  const int srow = (n0 + wave * WN) / kBlock;
+  const bool wave_live = (n0 + wave * WN) < N;
+
   u32x4 xreg[XCH];
   auto load_x = [&](int kt) {
-    const int kk = kt * kBK + xc * 8;
+    const bool kin = kt * kBK + xc * 8 < K;
+    const uint32_t base = kin ? xoff0 + (uint32_t)(kt * kBK * 2) : kOob;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int row = m0 + xr0 + 32 * i;
-      if (row < M && kk < K)
-        xreg[i] = *reinterpret_cast<const u32x4*>(x + (size_t)row * K + kk);
-      else
-        xreg[i] = u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < XCH; ++i)
+      xreg[i] = buf_load16(xrs, kin ? base + i * xrow_stride : kOob);
   };
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
       *reinterpret_cast<u32x4*>(&xs[buf][xs_offset(xr0 + 32 * i, xc)]) = xreg[i];
   };
-
-  // ---- W codes: lane holds 16 codes of row (lane % 32) of each column
-  // block, k chunk (lane / 32) of each 32-wide k slab.
-  const int wrow0 = n0 + wave * WN + (lane & 31);
-  const int wkoff = (lane >> 5) * 16;
-  u32x4 wreg[NB][2];
-  auto load_w = [&](int kt) {
+  auto load_w = [&](u32x4 (&wr)[NB][2], int kt) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int row = wrow0 + nb * 32;
+    for (int sl = 0; sl < 2; ++sl) {
+      const bool kin = kt * kBK + sl * 32 + wkoff < K;
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const int kk = kt * kBK + sl * 32 + wkoff;
-        if (row < N && kk < K)
-          wreg[nb][sl] = *reinterpret_cast<const u32x4*>(q + (size_t)row * K + kk);
-        else
-          wreg[nb][sl] = u32x4{0, 0, 0, 0};
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        wr[nb][sl] = buf_load16(wrs, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
+                                         : kOob);
     }
   };
-  const int srow = (n0 + wave * WN) / kBlock;
-  const bool wave_live = (n0 + wave * WN) < N;
+  auto scale_of = [&](int kt) -> float {
+    return wave_live ? s[srow * gk + (kt * kBK) / kBlock] : 0.0f;
+  };
+  // Dequantize the k16 step t of a code set into B operands.
+  auto decode_t = [&](bf16x8 (&wb)[NB][4], const u32x4 (&wr)[NB][2], float sc, int t) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      wb[nb][t] = dequant8(wr[nb][t >> 1][(t & 1) * 2], wr[nb][t >> 1][(t & 1) * 2 + 1], sc);
+  };
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -131,47 +170,47 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (kt0 < kt1) {
-    load_x(kt0);
-    load_w(kt0);
-    store_x(0);
-  }
-  __syncthreads();
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    // Dequantize this step's codes into MFMA B operands.
-    const float sc = wave_live ? s[srow * gk + (kt * kBK) / kBlock] : 0.0f;
-    bf16x8 wb[NB][4];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        wb[nb][sl * 2 + 0] = dequant8(wreg[nb][sl][0], wreg[nb][sl][1], sc);
-        wb[nb][sl * 2 + 1] = dequant8(wreg[nb][sl][2], wreg[nb][sl][3], sc);
-      }
-    // Prefetch the next step while this one computes.
-    const bool more = kt + 1 < kt1;
-    if (more) {
-      load_x(kt + 1);
-      load_w(kt + 1);
-    }
-    // k16 step t = slab * 2 + half; lane reads X row (l % 32), k chunk
-    // slab*32 + (l/32)*16 + half*8 -> 16-byte chunk index slab*4 + (l/32)*2 + half.
+  auto mfma_step = [&](int cur, bf16x8 (&wb)[NB][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int chunk = (t >> 1) * 4 + (lane >> 5) * 2 + (t & 1);
+      bf16x8 a[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = mb * 32 + (lane & 31);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[cur][xs_offset(row, chunk)]);
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(&xs[cur][xs_offset(mb * 32 + (lane & 31), chunk)]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wb[nb][t], acc[mb][nb], 0, 0, 0);
-      }
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb[nb][t], acc[mb][nb], 0, 0, 0);
     }
-    if (more) store_x(cur ^ 1);
+  };
+
+  {
+    // Decode this step's codes, prefetch the next step, then the MFMAs;
+    // the other resident workgroup's waves cover the decode.
+    u32x4 wr[NB][2];
+    bf16x8 wb[NB][4];
+    if (kt0 < kt1) {
+      load_x(kt0);
+      load_w(wr, kt0);
+      store_x(0);
+    }
     __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const float sc = scale_of(kt);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) decode_t(wb, wr, sc, t);
+      const bool has1 = kt + 1 < kt1;
+      if (has1) {
+        load_x(kt + 1);
+        load_w(wr, kt + 1);
+      }
+      mfma_step(cur, wb);
+      if (has1) store_x(cur ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- Epilogue. acc[mb][nb][r] holds row mb*32 + (r/4)*8 + (l/32)*4 + r%4,
@@ -195,6 +234,8 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
         }
       }
   } else {
+    // Split-K: this split's fp32 partial tile; a second kernel adds the
+    // splits in order and rounds once.
     float* p = part + (size_t)blockIdx.y * M * N;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -212,22 +253,34 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 }
 
 struct TiledPlan {
+  int cfg;          // 0: 128x256, 1: 256x128, 2: 128x128 (all 2 workgroups per CU)
   int bm, bn, splits, kt_per_split;
 };
 
+// Tile choice, from measurements on MI355X (fp8 weight, bf16 X):
+//  - M >= 2048: 128x256 tiles; four waves share a 128-row X tile and each
+//    decodes 64 weight rows.
+//  - smaller M with enough 256x128 tiles to cover every CU: 256x128, which
+//    halves the number of times each weight element is decoded.
+//  - otherwise 128x128 tiles with K split until there are >= ~512 work items
+//    (partials summed in split order by a second kernel).
 TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
   const int nkt = (int)((k + kBK - 1) / kBK);
-  TiledPlan p{256, 256, 1, nkt};
-  const int64_t tiles_big = ((m + 255) / 256) * ((n + 255) / 256);
-  if (tiles_big < 512) {
-    p.bm = 128;
-    p.bn = 128;
+  TiledPlan p{0, 128, 256, 1, nkt};
+  if (m < 2048) {
+    const int64_t t256 = ((m + 255) / 256) * ((n + 127) / 128);
+    if (t256 >= 256) {
+      p = TiledPlan{1, 256, 128, 1, nkt};
+    } else {
+      p = TiledPlan{2, 128, 128, 1, nkt};
+    }
   }
   const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + p.bn - 1) / p.bn);
-  // Too few tiles to fill 256 CUs: split K (partials summed in order).
+  // Too few tiles to occupy the GPU: split K until there are >= 512 work
+  // items (2 workgroups per CU), keeping >= 8 K steps per split. Measured
+  // best for the M=512 text-encoder shapes (4 splits of 128x128 tiles).
   int splits = 1;
-  while (tiles * splits < 200 && splits < 8 && nkt / (splits * 2) >= 8) splits *= 2;
-  p.splits = splits;
+  while (tiles * splits < 512 && splits < 8 && nkt / (splits * 2) >= 8) splits *= 2;
   p.kt_per_split = (nkt + splits - 1) / splits;
   p.splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
   return p;
@@ -235,6 +288,7 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
 
 }  // namespace
 
+// Workspace: the fp32 partials of every split.
 size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   const TiledPlan p = plan_tiled(m, n, k);
   if (p.splits <= 1) return 0;
@@ -248,12 +302,18 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
   const int gk = (int)((k + kBlock - 1) / kBlock);
   const int tiles_m = (int)((m + p.bm - 1) / p.bm);
   const int tiles_n = (int)((n + p.bn - 1) / p.bn);
-  float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
-  if (p.splits > 1 && (ws == nullptr || ws_bytes < tiled_workspace_bytes(m, n, k)))
-    return hipErrorInvalidValue;
+  float* part = nullptr;
+  if (p.splits > 1) {
+    if (ws == nullptr || ws_bytes < tiled_workspace_bytes(m, n, k)) return hipErrorInvalidValue;
+    part = static_cast<float*>(ws);
+  }
   const dim3 grid((uint32_t)(tiles_m * tiles_n), (uint32_t)p.splits);
-  if (p.bm == 256)
-    hipLaunchKernelGGL((gemm_tiled_kernel<256, 256, 1>), grid, dim3(kThreads), 0, stream,
+  if (p.cfg == 0)
+    hipLaunchKernelGGL((gemm_tiled_kernel<128, 256, 2>), grid, dim3(kThreads), 0, stream,
+                       x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
+                       p.kt_per_split);
+  else if (p.cfg == 1)
+    hipLaunchKernelGGL((gemm_tiled_kernel<256, 128, 2>), grid, dim3(kThreads), 0, stream,
                        x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
                        p.kt_per_split);
   else

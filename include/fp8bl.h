@@ -91,14 +91,15 @@ size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_t k);
  * plain matmul; LightX2V PR #1657, "Walkthrough": FP32 accumulation):
  *   y[m,n] = bf16_rne( sum_k x[m,k] * What[n,k] ),  What as in fp8_block_dequant,
  * with fp32 accumulation and one bf16 rounding per output. What is formed in
- * registers only. No bias.
+ * registers only. No bias. K may be at most 2^20.
  *   x          [m,k] bf16 bits  (in, 16-B aligned)
  *   q, scale_inv                (in, as above)
  *   y          [m,n] bf16 bits  (out, 16-B aligned, may not overlap)
  *   workspace  device scratch of at least fp8_block_linear_workspace_size
- *              bytes (256-B aligned), or NULL when that size is 0. Its contents
- *              need no initialisation and are not preserved. Two calls that
- *              share a workspace must be ordered (same stream). */
+ *              bytes (256-B aligned), or NULL when that size is 0 (it holds
+ *              fp32 split-K partials). Its contents need no initialisation
+ *              and are not preserved. Calls that share a workspace must be
+ *              ordered (same stream); calls that overlap on one workspace race. */
 int fp8_block_linear(const uint16_t* x, const uint8_t* q, const float* scale_inv,
                      uint16_t* y, int64_t m, int64_t n, int64_t k,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);

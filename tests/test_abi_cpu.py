@@ -42,7 +42,7 @@ def test_workspace_sizes():
                     (16384, 3072, 3072), (3, 100, 4096), (512, 5120, 25600)]:
         ws = L.workspace_size(m, n, k)
         assert ws % 256 == 0
-        assert ws <= 16 * m * n * 4 + 256
+        assert ws <= 8 * m * n * 4 + 256
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced here
@@ -65,6 +65,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced here
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),        # y overlaps x
     ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 7), L.FP8BL_INVALID_ARG),    # bad path
     ((FAKE, FAKE, FAKE, 4 * FAKE, 1 << 31, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),  # M too big
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 1, 8, (1 << 20) + 16, 0, 0, 0), L.FP8BL_INVALID_ARG),  # K too big
     ((FAKE, FAKE, FAKE, 4 * FAKE, 0, 8, 16, 0, 0, 0), L.FP8BL_OK),             # empty M: no-op
     ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 0, 16, 0, 0, 0), L.FP8BL_OK),             # empty N: no-op
     ((0, 0, 0, 0, 0, 0, 16, 0, 0, 0), L.FP8BL_OK),                             # empty, null ok

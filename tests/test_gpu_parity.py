@@ -230,6 +230,50 @@ def test_linear_reproducible(path):
     assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
 
 
+def test_linear_shared_workspace_reused():
+    """Split-K shapes of several sizes through one workspace filled with
+    garbage, twice: the partials need no initialisation and every result
+    stays within the bound."""
+    shapes = [(512, 256, 2048), (130, 513, 528), (64, 384, 4096), (512, 640, 5120)]
+    need = max(F.workspace_size(m, n, k) for m, n, k in shapes)
+    assert need > 0
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda:0")
+    for rep in range(2):
+        for m, n, k in shapes:
+            x, w = random_problem(m + n + k + rep, m, n, k)
+            q, s = O.quantize(w)
+            say("shared workspace", rep, m, n, k)
+            y = F.fp8_block_linear(to_bf16(x), to_u8(q), to_f32(s), workspace=ws,
+                                   path=F.PATH_TILED)
+            torch.cuda.synchronize()
+            yr, ar = O.linear_exact(x, O.dequant(q, s))
+            assert_bound(bits(y), yr, ar, f"shared ws {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 640, 5120), (16, 8000, 1024), (300, 1024, 512)])
+def test_linear_graph_replay_matches_eager(m, n, k):
+    """The call captured into a HIP graph and replayed several times, with
+    eager work and synchronisations between replays, gives the eager bits
+    every time (split-K and skinny shapes included)."""
+    x, w = random_problem(m * 3 + n + k, m, n, k)
+    q, s = O.quantize(w)
+    xt, qt, st = to_bf16(x), to_u8(q), to_f32(s)
+    ws = torch.empty(max(F.workspace_size(m, n, k), 1), dtype=torch.uint8, device="cuda:0")
+    say("graph replay", m, n, k)
+    eager = bits(F.fp8_block_linear(xt, qt, st, workspace=ws))
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        F.fp8_block_linear(xt, qt, st, out=out, workspace=ws)
+    for rep in range(3):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), rep
+        F.fp8_block_linear(xt, qt, st, workspace=ws)     # eager work in between
+        torch.cuda.synchronize()
+
+
 def test_linear_empty_shapes():
     say("empty shapes")
     q = to_u8(np.zeros((8, 32), np.uint8))
