@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0 = auto)")
+    ap.add_argument("--op", default="linear", choices=["linear", "dequant", "quantize"],
+                    help="linear (default): the fused layer; dequant / quantize: the "
+                         "standalone kernels on the workload's weight")
     ap.add_argument("--eager", action="store_true",
                     help="time K separate calls instead of one replay of a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -174,9 +177,19 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    if args.op == "dequant":
+        wouts = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
+    if args.op == "quantize":
+        w_srcs = [torch.from_numpy(lin.w).to(dev) for _ in range(min(rotate, 4))]
+
     def step(i):
         x, q, s, y = sets[i % rotate]
-        F.fp8_block_linear(x, q, s, out=y, workspace=ws)
+        if args.op == "linear":
+            F.fp8_block_linear(x, q, s, out=y, workspace=ws)
+        elif args.op == "dequant":
+            F.fp8_block_dequant(q, s, out=wouts[i % rotate])
+        else:
+            F.fp8_block_quantize(w_srcs[i % len(w_srcs)], q, s)
 
     for i in range(args.warmup):
         step(i)
@@ -217,6 +230,11 @@ def main():
 
     flops = 2.0 * m * n * k
     abytes = alg_bytes(m, n, k)
+    gn, gk = -(-n // 128), -(-k // 128)
+    if args.op == "dequant":          # 1 B code in, 2 B bf16 out, plus the scale grid
+        bound, flops, abytes = "hbm", 0.0, 3 * n * k + 4 * gn * gk
+    elif args.op == "quantize":       # 4 B fp32 in, 1 B code out, plus the scale grid
+        bound, flops, abytes = "hbm", 0.0, 5 * n * k + 4 * gn * gk
     if bound == "hbm":
         unit, value = "GB/s", abytes * args.steps / wall / 1e9
         achieved, peak, r_unit = abytes / avg_launch_s / 1e9, HBM_PEAK_GBPS, "GB/s"
@@ -237,7 +255,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "m": m, "n": n, "k": k,
+        "config": {"workload": args.workload, "op": args.op, "m": m, "n": n, "k": k,
                    "weight": "e4m3 + fp32 128x128 scale_inv", "rotated_sets": rotate,
                    "launch": "eager" if args.eager else "hip graph of K steps",
                    "parallelism": "none (1 GPU)"},
@@ -247,13 +265,13 @@ def main():
             "peak": peak,
             "unit": r_unit,
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload if args.op == "linear" else f"{args.op}:{args.workload}"),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
             "alg_bytes": abytes,
             "flops": flops,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "linear":
         cb = cpu_baseline(lin, x_bits)
         if bound == "hbm":
             # oracle throughput expressed in the metric's unit (bytes of the sample)

@@ -276,11 +276,14 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
     }
   }
   const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + p.bn - 1) / p.bn);
-  // Too few tiles to occupy the GPU: split K until there are >= 512 work
-  // items (2 workgroups per CU), keeping >= 8 K steps per split. Measured
-  // best for the M=512 text-encoder shapes (4 splits of 128x128 tiles).
+  // Fewer tiles than CUs: split K until there are >= 512 work items (2
+  // workgroups per CU), keeping >= 8 K steps per split. Measured on the
+  // M=512 text-encoder shapes: 160 tiles of 128x128 run best as 4 splits,
+  // while 400 tiles of 256x128 run best unsplit (the partials' round trip
+  // costs more than the idle slots).
   int splits = 1;
-  while (tiles * splits < 512 && splits < 8 && nkt / (splits * 2) >= 8) splits *= 2;
+  if (tiles < 256)
+    while (tiles * splits < 512 && splits < 8 && nkt / (splits * 2) >= 8) splits *= 2;
   p.kt_per_split = (nkt + splits - 1) / splits;
   p.splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
   return p;
