@@ -26,12 +26,15 @@ hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* 
                               uint16_t* y, int64_t m, int64_t n, int64_t k,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
-// Deterministic sum of `splits` fp32 partial [M,N] slabs (in split order)
-// and one bf16 rounding into y.
+// Deterministic sum of `splits` fp32 partial [M,N] slabs (in split order,
+// slab stride partial_slab(M, N)) and one bf16 rounding into y.
 hipError_t launch_reduce_partials(const float* part, uint16_t* y, int splits,
                                   int64_t m, int64_t n, hipStream_t stream);
 
 constexpr size_t kWorkspaceAlign = 256;
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// Split-K partial slabs ([M,N] fp32 each) start every 64 floats, so every
+// slab is 256-byte aligned inside the workspace.
+__host__ __device__ inline size_t partial_slab(size_t m, size_t n) { return (m * n + 63) & ~(size_t)63; }
 
 }  // namespace fp8bl

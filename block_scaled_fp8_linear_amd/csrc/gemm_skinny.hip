@@ -217,20 +217,38 @@ void gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
       const __bf16 v = (__bf16)t[r];
       y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, v);
     } else {
-      part[((size_t)blockIdx.y * M + row) * N + col] = t[r];
+      part[(size_t)blockIdx.y * partial_slab(M, N) + (size_t)row * N + col] = t[r];
     }
   }
 }
 
+// Sum of split-K partials, 8 outputs per thread (two 16-byte loads per
+// split), added in split order and rounded once; a scalar tail handles
+// M*N not divisible by 8.
 __global__ __launch_bounds__(256)
 void reduce_partials_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
-                            int splits, size_t mn) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= mn) return;
-  float t = part[i];
-  for (int sp = 1; sp < splits; ++sp) t += part[(size_t)sp * mn + i];
-  const __bf16 v = (__bf16)t;
-  y[i] = __builtin_bit_cast(uint16_t, v);
+                            int splits, size_t mn, size_t slab) {
+  const size_t i8 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i8 + 8 <= mn) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + i8);
+    f32x4 b = *reinterpret_cast<const f32x4*>(part + i8 + 4);
+    for (int sp = 1; sp < splits; ++sp) {
+      const f32x4 c = *reinterpret_cast<const f32x4*>(part + (size_t)sp * slab + i8);
+      const f32x4 d = *reinterpret_cast<const f32x4*>(part + (size_t)sp * slab + i8 + 4);
+      a[0] += c[0]; a[1] += c[1]; a[2] += c[2]; a[3] += c[3];
+      b[0] += d[0]; b[1] += d[1]; b[2] += d[2]; b[3] += d[3];
+    }
+    u32x4 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+               pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+    *reinterpret_cast<u32x4*>(y + i8) = o;
+  } else {
+    for (size_t i = i8; i < mn; ++i) {
+      float t = part[i];
+      for (int sp = 1; sp < splits; ++sp) t += part[(size_t)sp * slab + i];
+      const __bf16 v = (__bf16)t;
+      y[i] = __builtin_bit_cast(uint16_t, v);
+    }
+  }
 }
 
 constexpr int kWaves = 4;
@@ -263,9 +281,9 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k) {
 hipError_t launch_reduce_partials(const float* part, uint16_t* y, int splits,
                                   int64_t m, int64_t n, hipStream_t stream) {
   const size_t mn = (size_t)m * (size_t)n;
-  const size_t blocks = (mn + 255) / 256;
+  const size_t blocks = (mn + 256 * 8 - 1) / (256 * 8);
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     part, y, splits, mn);
+                     part, y, splits, mn, partial_slab((size_t)m, (size_t)n));
   return hipGetLastError();
 }
 
@@ -276,7 +294,7 @@ size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (rows == 0) return 0;
   const SkinnyPlan p = plan_skinny(rows, n, k);
   if (p.splits <= 1) return 0;
-  return round_up((size_t)p.splits * (size_t)rows * (size_t)n * sizeof(float), kWorkspaceAlign);
+  return round_up((size_t)p.splits * partial_slab(rows, n) * sizeof(float), kWorkspaceAlign);
 }
 
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* s,
@@ -287,7 +305,7 @@ hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* 
     const int64_t rows = (m - r0) < 32 ? (m - r0) : 32;
     const SkinnyPlan p = plan_skinny(rows, n, k);
     float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
-    if (p.splits > 1 && (ws == nullptr || ws_bytes < (size_t)p.splits * rows * n * sizeof(float)))
+    if (p.splits > 1 && (ws == nullptr || ws_bytes < (size_t)p.splits * partial_slab(rows, n) * sizeof(float)))
       return hipErrorInvalidValue;
     const dim3 grid((uint32_t)((n + 16 * p.nt - 1) / (16 * p.nt)), (uint32_t)p.splits);
     const uint16_t* xp = x + (size_t)r0 * k;

@@ -131,7 +131,7 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 
   u32x4 xreg[XCH];
   auto load_x = [&](int kt) {
-    const bool kin = kt * kBK + xc * 8 < K;
+    const bool kin = kt < kt1 && kt * kBK + xc * 8 < K;
     const uint32_t base = kin ? xoff0 + (uint32_t)(kt * kBK * 2) : kOob;
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
@@ -145,7 +145,7 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   auto load_w = [&](u32x4 (&wr)[NB][2], int kt) {
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
-      const bool kin = kt * kBK + sl * 32 + wkoff < K;
+      const bool kin = kt < kt1 && kt * kBK + sl * 32 + wkoff < K;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         wr[nb][sl] = buf_load16(wrs, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
@@ -153,7 +153,10 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     }
   };
   auto scale_of = [&](int kt) -> float {
-    return wave_live ? s[srow * gk + (kt * kBK) / kBlock] : 0.0f;
+    // always a valid address (clamped block column), zero for dead waves
+    const int kb = min((kt * kBK) / kBlock, gk - 1);
+    const float v = s[(wave_live ? srow : 0) * gk + kb];
+    return wave_live ? v : 0.0f;
   };
   // Dequantize the k16 step t of a code set into B operands.
   auto decode_t = [&](bf16x8 (&wb)[NB][4], const u32x4 (&wr)[NB][2], float sc, int t) {
@@ -202,13 +205,16 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
       const float sc = scale_of(kt);
 #pragma unroll
       for (int t = 0; t < 4; ++t) decode_t(wb, wr, sc, t);
-      const bool has1 = kt + 1 < kt1;
-      if (has1) {
-        load_x(kt + 1);
-        load_w(wr, kt + 1);
-      }
+      // Branch-free step (one basic block for the scheduler): past the last
+      // step these loads read zero and the staged tile goes unused.
+      load_x(kt + 1);
+      load_w(wr, kt + 1);
+      // Raise this wave's issue priority while it feeds the matrix core, so
+      // the other workgroup's decode fills VALU slots around it.
+      __builtin_amdgcn_s_setprio(1);
       mfma_step(cur, wb);
-      if (has1) store_x(cur ^ 1);
+      __builtin_amdgcn_s_setprio(0);
+      store_x(cur ^ 1);
       __syncthreads();
     }
   }
@@ -236,7 +242,7 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   } else {
     // Split-K: this split's fp32 partial tile; a second kernel adds the
     // splits in order and rounds once.
-    float* p = part + (size_t)blockIdx.y * M * N;
+    float* p = part + (size_t)blockIdx.y * partial_slab(M, N);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -295,7 +301,7 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
 size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   const TiledPlan p = plan_tiled(m, n, k);
   if (p.splits <= 1) return 0;
-  return round_up((size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), kWorkspaceAlign);
+  return round_up((size_t)p.splits * partial_slab(m, n) * sizeof(float), kWorkspaceAlign);
 }
 
 hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s,
