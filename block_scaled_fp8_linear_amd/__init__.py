@@ -6,7 +6,7 @@ MiniMax H3: block-FP8 text encoder on Hopper, its converter, and a 4xH100
 FastH3 profile", "Changes"). The library behind this module (libfp8bl.so,
 hand-written HIP) provides:
 
-* ``fp8_block_quantize(w)``  -> (q, s)     the converter's quantization
+* ``fp8_block_quantize(w)``  -> (q, s)     the converter's quantization (fp32 or bf16 w)
 * ``fp8_block_dequant(q, s)`` -> bf16 W_hat  bit-exact dequant
 * ``fp8_block_linear(x, q, s)`` -> bf16 Y = X W_hat^T, fp32 accumulation
 
@@ -59,8 +59,10 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 def fp8_block_quantize(w: torch.Tensor, q: torch.Tensor | None = None,
                        s: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
-    """fp32 w [N,K] -> (q uint8 [N,K], s fp32 [ceil(N/128), ceil(K/128)])."""
-    _need(w, torch.float32, "w")
+    """fp32 or bf16 w [N,K] -> (q uint8 [N,K], s fp32 [ceil(N/128), ceil(K/128)])."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"w must be float32 or bfloat16, got {w.dtype}")
+    _need(w, w.dtype, "w")
     n, k = w.shape
     if q is None:
         q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
@@ -70,9 +72,10 @@ def fp8_block_quantize(w: torch.Tensor, q: torch.Tensor | None = None,
     _need(s, torch.float32, "s")
     if tuple(q.shape) != (n, k) or tuple(s.shape) != scale_grid_shape(n, k):
         raise ValueError("output shapes do not match w")
+    raw = _lib.quantize_raw if w.dtype == torch.float32 else _lib.quantize_bf16_raw
     with torch.cuda.device(w.device):
-        _check(_lib.quantize_raw(w.data_ptr(), q.data_ptr(), s.data_ptr(), n, k,
-                                 _stream(w.device)), "fp8_block_quantize")
+        _check(raw(w.data_ptr(), q.data_ptr(), s.data_ptr(), n, k, _stream(w.device)),
+               "fp8_block_quantize")
     return q, s
 
 

@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_linear_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, c_int, vp]
     lib.fp8_block_quantize.restype = c_int
     lib.fp8_block_quantize.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.fp8_block_quantize_bf16.restype = c_int
+    lib.fp8_block_quantize_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
     _lib = lib
     return lib
 
@@ -102,3 +104,7 @@ def linear_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,
 
 def quantize_raw(w: int, q: int, s: int, n: int, k: int, stream: int = 0) -> int:
     return load().fp8_block_quantize(w, q, s, n, k, stream)
+
+
+def quantize_bf16_raw(w: int, q: int, s: int, n: int, k: int, stream: int = 0) -> int:
+    return load().fp8_block_quantize_bf16(w, q, s, n, k, stream)

@@ -16,7 +16,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;     // every dimension fits int32
-constexpr int64_t kMaxElems = (int64_t)1 << 36;   // N*K and M*N (16-byte chunk index fits uint32)
+constexpr int64_t kMaxElems = (int64_t)1 << 35;   // N*K, M*K and M*N (8-element chunk index fits uint32)
 constexpr int kSkinnyMaxM = 32;
 // The GEMM kernels address a tile's rows with 32-bit buffer offsets.
 constexpr int64_t kMaxLinearK = (int64_t)1 << 20;
@@ -177,4 +177,21 @@ FP8BL_EXPORT int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv
   st = gate_current_device();
   if (st != FP8BL_OK) return st;
   return hip_status(fp8bl::launch_quantize(w, q, scale_inv, n, k, stream));
+}
+
+FP8BL_EXPORT int fp8_block_quantize_bf16(const uint16_t* w_bf16, uint8_t* q, float* scale_inv,
+                                         int64_t n, int64_t k, hipStream_t stream) {
+  int st = check_nk(n, k);
+  if (st != FP8BL_OK) return st;
+  if (n == 0) return FP8BL_OK;
+  if ((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK > 65535 * 4) return FP8BL_INVALID_ARG;
+  if (!w_bf16 || !q || !scale_inv) return FP8BL_INVALID_ARG;
+  if (!aligned(w_bf16, 16) || !aligned(q, 16) || !aligned(scale_inv, 4)) return FP8BL_ALIGNMENT;
+  const size_t sbytes = grid_elems(n, k) * 4;
+  if (overlap(q, (size_t)n * k, w_bf16, (size_t)n * k * 2) ||
+      overlap(scale_inv, sbytes, w_bf16, (size_t)n * k * 2) || overlap(q, (size_t)n * k, scale_inv, sbytes))
+    return FP8BL_INVALID_ARG;
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_quantize_bf16(w_bf16, q, scale_inv, n, k, stream));
 }

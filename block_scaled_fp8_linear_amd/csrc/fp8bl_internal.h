@@ -13,6 +13,8 @@ hipError_t launch_dequant(const uint8_t* q, const float* s, uint16_t* w,
 
 hipError_t launch_quantize(const float* w, uint8_t* q, float* s,
                            int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_quantize_bf16(const uint16_t* w, uint8_t* q, float* s,
+                                int64_t n, int64_t k, hipStream_t stream);
 
 // Large-M fused GEMM (E4M3 tiles decoded to bf16 in registers, bf16 MFMA).
 size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k);

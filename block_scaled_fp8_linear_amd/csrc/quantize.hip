@@ -7,7 +7,8 @@
 //   code = nearest finite E4M3 to fl32(w / S), ties to the even code,
 //          saturating at 448, sign kept.
 // One workgroup per block; offline work, so it favours exactness over speed
-// (two IEEE divisions per element).
+// (two IEEE divisions per element). The input is fp32, or bf16 widened
+// exactly to fp32 (a checkpoint stored in bf16).
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
@@ -40,8 +41,20 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float v) {
 
 constexpr int kThreads = 256;
 
+// Four consecutive inputs as fp32: fp32 loads as they are; bf16 widens
+// exactly (its 16 bits are the high half of the fp32 pattern).
+__device__ __forceinline__ f32x4 load4(const float* w, size_t i) {
+  return *reinterpret_cast<const f32x4*>(w + i);
+}
+__device__ __forceinline__ f32x4 load4(const uint16_t* w, size_t i) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(w + i);
+  return f32x4{__builtin_bit_cast(float, v[0] << 16), __builtin_bit_cast(float, v[0] & 0xFFFF0000u),
+               __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xFFFF0000u)};
+}
+
+template <typename T>
 __global__ __launch_bounds__(kThreads)
-void quantize_kernel(const float* __restrict__ w, uint8_t* __restrict__ q,
+void quantize_kernel(const T* __restrict__ w, uint8_t* __restrict__ q,
                      float* __restrict__ s, int N, int K, int gk) {
   __shared__ float wave_max[kThreads / 64];
   const int bi = blockIdx.y, bj = blockIdx.x;
@@ -57,7 +70,7 @@ void quantize_kernel(const float* __restrict__ w, uint8_t* __restrict__ q,
   for (int c = 0; c < 16; ++c) {
     const int col = col0 + c * 4;
     if (row_ok && col < K) {
-      v[c] = *reinterpret_cast<const f32x4*>(w + (size_t)row * K + col);
+      v[c] = load4(w, (size_t)row * K + col);
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])),
                                fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
     } else {
@@ -95,7 +108,16 @@ hipError_t launch_quantize(const float* w, uint8_t* q, float* s, int64_t n, int6
                            hipStream_t stream) {
   const int gn = (int)((n + kBlock - 1) / kBlock);
   const int gk = (int)((k + kBlock - 1) / kBlock);
-  hipLaunchKernelGGL(quantize_kernel, dim3((uint32_t)gk, (uint32_t)gn), dim3(kThreads), 0,
+  hipLaunchKernelGGL(quantize_kernel<float>, dim3((uint32_t)gk, (uint32_t)gn), dim3(kThreads), 0,
+                     stream, w, q, s, (int)n, (int)k, gk);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_bf16(const uint16_t* w, uint8_t* q, float* s, int64_t n, int64_t k,
+                                hipStream_t stream) {
+  const int gn = (int)((n + kBlock - 1) / kBlock);
+  const int gk = (int)((k + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((uint32_t)gk, (uint32_t)gn), dim3(kThreads), 0,
                      stream, w, q, s, (int)n, (int)k, gk);
   return hipGetLastError();
 }

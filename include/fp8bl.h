@@ -18,7 +18,8 @@
  *     is enqueued on `stream` (NULL = the default stream) and the call returns.
  *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
  *   - Row-major, contiguous. Dimensions are int64_t; zero rows or columns is a
- *     no-op that returns FP8BL_OK. K must be a positive multiple of 16.
+ *     no-op that returns FP8BL_OK. K must be a positive multiple of 16; each
+ *     dimension is below 2^31 and each matrix has at most 2^35 elements.
  *   - Data pointers must be 16-byte aligned (scale grids 4-byte aligned,
  *     workspaces 256-byte aligned). Outputs must not overlap inputs.
  *   - Every argument error is reported by the return code BEFORE anything is
@@ -123,6 +124,13 @@ int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_
  * Bit-exact. Non-finite w gives unspecified codes and scales. */
 int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,
                        int64_t n, int64_t k, hipStream_t stream);
+
+/* fp8_block_quantize for a bf16 weight (the converter reading a bf16
+ * checkpoint): each element is widened exactly to fp32, then quantized as
+ * above. Same outputs, contract and bit-exactness.
+ *   w_bf16     [n,k] bf16 bits, finite (in, 16-B aligned) */
+int fp8_block_quantize_bf16(const uint16_t* w_bf16, uint8_t* q, float* scale_inv,
+                            int64_t n, int64_t k, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,6 +41,7 @@ from .fp8_block_ref import (  # noqa: F401
     e4m3_encode_nearest,
     e4m3_encode_bits,
     quantize,
+    quantize_bf16,
     linear_exact,
     linear_value,
     linear_sampled,

@@ -227,6 +227,13 @@ def quantize(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
+def quantize_bf16(w_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """The converter reading a bf16 weight: every bf16 value is exactly an
+    fp32 value, so the block quantization is the fp32 one on the widened
+    weight."""
+    return quantize(bf16_bits_to_f32(w_bits))
+
+
 # ---------------------------------------------------------------------------
 # Linear.  FastVideo PR #1829, "Purpose": a plain matmul of the dequantized
 # bf16 weight, Y = X W_hat^T; LightX2V PR #1657 "Walkthrough": accumulation in

@@ -19,7 +19,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "fp8_block_abi_version", "fp8_block_status_string", "fp8_block_device_supported",
         "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
-        "fp8_block_linear_ex", "fp8_block_quantize",
+        "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
     }
     for name in names:
         assert hasattr(lib, name), name
@@ -111,7 +111,8 @@ def test_valid_call_without_gpu_reports_device_status(lib):
 def test_dequant_and_quantize_argument_errors(lib, n, k, qoff, soff, woff, status):
     q, s, w = FAKE + qoff, 8 * FAKE + soff, 16 * FAKE + woff
     assert L.dequant_raw(q, s, w, n, k) == status
-    # quantize(w, q, s): w is the fp32 input
+    # quantize(w, q, s): w is the fp32 (or bf16) input
     assert L.quantize_raw(w, q, s, n, k) == status
+    assert L.quantize_bf16_raw(w, q, s, n, k) == status
     # overlapping output
     assert L.dequant_raw(FAKE, 8 * FAKE, FAKE, 8, 16) == L.FP8BL_INVALID_ARG

@@ -131,6 +131,20 @@ def test_quantize_ragged(n, k, std):
     assert np.array_equal(u8(qt), q)
 
 
+@pytest.mark.parametrize("n,k", [(384, 256), (5120, 5120), (200, 160), (1, 16), (129, 272)])
+def test_quantize_bf16_input(n, k):
+    _, w = random_problem(n * 5 + k, 1, n, k)
+    bits_w = O.bf16_rne_bits(w)
+    if n > 128 and k > 128:
+        bits_w[128:256, 128:256] = 0                                  # an all-zero block
+    say("quantize bf16 input", n, k)
+    qt, st = F.fp8_block_quantize(to_bf16(bits_w))
+    torch.cuda.synchronize()
+    q, s = O.quantize_bf16(bits_w)
+    assert np.array_equal(f32(st).view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(u8(qt), q)
+
+
 def test_quantize_subnormal_and_tie_values():
     """Values placed on E4M3 midpoints (ties) and deep in the subnormal
     range of both formats, after the per-block scale is applied."""

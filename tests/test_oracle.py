@@ -371,6 +371,26 @@ def test_full_round_trip_within_e4m3_precision():
     assert rel.max() <= 2.0 ** -4 + 2.0 ** -8
 
 
+def test_quantize_bf16_input_pins():
+    """bf16 weights: the widening used by the oracle agrees with the
+    library's bfloat16 -> float32 cast, and the quantized blocks keep the
+    invariants (scale = fl32(amax/448), a +-448 code per non-zero block)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    w32 = (rng.standard_normal((200, 272)) * 0.05).astype(np.float32)
+    bits = O.bf16_rne_bits(w32)
+    widened = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(widened.view(np.uint32), O.bf16_bits_to_f32(bits).view(np.uint32))
+    q, s = O.quantize_bf16(bits)
+    q2, s2 = O.quantize(widened)
+    assert np.array_equal(q, q2) and np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+    for i in range(2):
+        for j in range(3):
+            blk = widened[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128].astype(np.float64)
+            assert s[i, j] == np.float32(np.max(np.abs(blk)) / 448.0)
+            assert np.any((q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128] & 0x7F) == 0x7E)
+
+
 # ---------------------------------------------------------------------------
 # Linear (fp64 matmul) and the bound
 # ---------------------------------------------------------------------------
