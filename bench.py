@@ -119,9 +119,10 @@ def main():
     ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0 = auto)")
-    ap.add_argument("--op", default="linear", choices=["linear", "dequant", "quantize"],
+    ap.add_argument("--op", default="linear", choices=["linear", "dequant", "quantize", "mlp"],
                     help="linear (default): the fused layer; dequant / quantize: the "
-                         "standalone kernels on the workload's weight")
+                         "standalone kernels on the workload's weight; mlp: the gate/up "
+                         "pair with the SwiGLU epilogue in one launch (workload mlp_gate)")
     ap.add_argument("--eager", action="store_true",
                     help="time K separate calls instead of one replay of a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -149,6 +150,9 @@ def main():
     import block_scaled_fp8_linear_amd as F
     from workloads import generate
 
+    if args.op == "mlp" and args.workload != "mlp_gate":
+        print("--op mlp runs on the gate/up pair: use --workload mlp_gate", file=sys.stderr)
+        sys.exit(2)
     gen_name, idx, bound = WORKLOADS[args.workload]
     wl = generate(gen_name)
     lin = wl.linears[idx]
@@ -162,6 +166,8 @@ def main():
     if not F.device_supported(0):
         raise RuntimeError("cuda:0 is not a gfx950 device")
     set_bytes = 2 * m * k + n * k + 2 * m * n
+    if args.op == "mlp":
+        set_bytes += n * k
     rotate = args.rotate or int(min(64, max(1, -(-2 * MALL_BYTES // set_bytes))))
 
     w_dev = torch.from_numpy(lin.w).to(dev)
@@ -173,6 +179,11 @@ def main():
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         sets.append((x, q, s, y))
     del w_dev
+    if args.op == "mlp":
+        # the up weight of the pair, one copy per set like the gate weight
+        wu_dev = torch.from_numpy(wl.linears[idx + 1].w).to(dev)
+        ups = [F.fp8_block_quantize(wu_dev) for _ in range(rotate)]
+        del wu_dev
     ws_bytes = F.workspace_size(m, n, k)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -186,6 +197,9 @@ def main():
         x, q, s, y = sets[i % rotate]
         if args.op == "linear":
             F.fp8_block_linear(x, q, s, out=y, workspace=ws)
+        elif args.op == "mlp":
+            qu, su = ups[i % rotate]
+            F.fp8_block_mlp_gate_up(x, q, s, qu, su, out=y)
         elif args.op == "dequant":
             F.fp8_block_dequant(q, s, out=wouts[i % rotate])
         else:
@@ -235,6 +249,9 @@ def main():
         bound, flops, abytes = "hbm", 0.0, 3 * n * k + 4 * gn * gk
     elif args.op == "quantize":       # 4 B fp32 in, 1 B code out, plus the scale grid
         bound, flops, abytes = "hbm", 0.0, 5 * n * k + 4 * gn * gk
+    elif args.op == "mlp":            # two products over one X, one bf16 output
+        flops = 4.0 * m * n * k
+        abytes = 2 * m * k + 2 * (n * k + 4 * gn * gk) + 2 * m * n
     if bound == "hbm":
         unit, value = "GB/s", abytes * args.steps / wall / 1e9
         achieved, peak, r_unit = abytes / avg_launch_s / 1e9, HBM_PEAK_GBPS, "GB/s"

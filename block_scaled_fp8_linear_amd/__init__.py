@@ -9,6 +9,8 @@ hand-written HIP) provides:
 * ``fp8_block_quantize(w)``  -> (q, s)     the converter's quantization (fp32 or bf16 w)
 * ``fp8_block_dequant(q, s)`` -> bf16 W_hat  bit-exact dequant
 * ``fp8_block_linear(x, q, s)`` -> bf16 Y = X W_hat^T, fp32 accumulation
+* ``fp8_block_mlp_gate_up(x, qg, sg, qu, su)`` -> bf16 swiglu(X Wg^T, X Wu^T)
+  in one launch (the MLP's gate/up pair)
 
 The functions here only marshal torch tensors (device memory and the current
 stream) into the C ABI declared in include/fp8bl.h; all arithmetic runs in
@@ -29,7 +31,8 @@ from ._lib import (  # noqa: F401
 BLOCK = 128
 
 __all__ = [
-    "fp8_block_quantize", "fp8_block_dequant", "fp8_block_linear", "workspace_size",
+    "fp8_block_quantize", "fp8_block_dequant", "fp8_block_linear", "fp8_block_mlp_gate_up",
+    "workspace_size",
     "device_supported", "abi_version", "status_string", "Fp8blError",
     "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "scale_grid_shape",
 ]
@@ -129,4 +132,33 @@ def fp8_block_linear(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
         _check(_lib.linear_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), out.data_ptr(),
                                m, n, k, ws_ptr, ws_bytes, path, _stream(x.device)),
                "fp8_block_linear")
+    return out
+
+
+def fp8_block_mlp_gate_up(x: torch.Tensor, q_gate: torch.Tensor, s_gate: torch.Tensor,
+                          q_up: torch.Tensor, s_up: torch.Tensor,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 x [M,K] and two block-FP8 weights [N,K] -> bf16 h [M,N] with
+    h = bf16(bf16(silu(g)) * u), g and u the two linears' bf16 outputs."""
+    _need(x, torch.bfloat16, "x")
+    for t, name in ((q_gate, "q_gate"), (q_up, "q_up")):
+        _need(t, torch.uint8, name)
+    for t, name in ((s_gate, "s_gate"), (s_up, "s_up")):
+        _need(t, torch.float32, name)
+    m, k = x.shape
+    n, kq = q_gate.shape
+    if kq != k or tuple(q_up.shape) != (n, k):
+        raise ValueError(f"weights must both be [{n}, {k}] to match x")
+    grid = scale_grid_shape(n, k)
+    if tuple(s_gate.shape) != grid or tuple(s_up.shape) != grid:
+        raise ValueError(f"scale grids must be {grid}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out shape")
+    with torch.cuda.device(x.device):
+        _check(_lib.mlp_gate_up_raw(x.data_ptr(), q_gate.data_ptr(), s_gate.data_ptr(),
+                                    q_up.data_ptr(), s_up.data_ptr(), out.data_ptr(),
+                                    m, n, k, _stream(x.device)), "fp8_block_mlp_gate_up")
     return out

@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
     lib.fp8_block_linear_ex.restype = c_int
     lib.fp8_block_linear_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, c_int, vp]
+    lib.fp8_block_mlp_gate_up.restype = c_int
+    lib.fp8_block_mlp_gate_up.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_block_quantize.restype = c_int
     lib.fp8_block_quantize.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fp8_block_quantize_bf16.restype = c_int
@@ -100,6 +102,11 @@ def dequant_raw(q: int, s: int, w: int, n: int, k: int, stream: int = 0) -> int:
 def linear_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,
                ws: int, ws_bytes: int, path: int = PATH_AUTO, stream: int = 0) -> int:
     return load().fp8_block_linear_ex(x, q, s, y, m, n, k, ws, ws_bytes, path, stream)
+
+
+def mlp_gate_up_raw(x: int, qg: int, sg: int, qu: int, su: int, h: int,
+                    m: int, n: int, k: int, stream: int = 0) -> int:
+    return load().fp8_block_mlp_gate_up(x, qg, sg, qu, su, h, m, n, k, stream)
 
 
 def quantize_raw(w: int, q: int, s: int, n: int, k: int, stream: int = 0) -> int:

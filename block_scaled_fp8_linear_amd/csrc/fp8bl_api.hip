@@ -162,6 +162,21 @@ FP8BL_EXPORT int fp8_block_linear(const uint16_t* x, const uint8_t* q, const flo
                              FP8BL_PATH_AUTO, stream);
 }
 
+FP8BL_EXPORT int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate,
+                                       const float* scale_inv_gate, const uint8_t* q_up,
+                                       const float* scale_inv_up, uint16_t* h, int64_t m,
+                                       int64_t n, int64_t k, hipStream_t stream) {
+  int st = validate_linear(x, q_gate, scale_inv_gate, h, m, n, k, FP8BL_PATH_AUTO);
+  if (st != FP8BL_OK) return st;
+  st = validate_linear(x, q_up, scale_inv_up, h, m, n, k, FP8BL_PATH_AUTO);
+  if (st != FP8BL_OK) return st;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_mlp_gate_up(x, q_gate, scale_inv_gate, q_up, scale_inv_up, h,
+                                              m, n, k, stream));
+}
+
 FP8BL_EXPORT int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,
                                     int64_t n, int64_t k, hipStream_t stream) {
   int st = check_nk(n, k);

@@ -22,6 +22,11 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
                              uint16_t* y, int64_t m, int64_t n, int64_t k,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+// MLP gate/up pair with the SwiGLU epilogue: h = swiglu(x Wg^T, x Wu^T).
+hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
+                              const uint8_t* qu, const float* su, uint16_t* h,
+                              int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
 // Skinny-M (M <= 32 rows per pass) weight-streaming GEMM.
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* s,

@@ -71,12 +71,29 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int BM, int BN, int MINB>
+// bf16 SwiGLU of two fp32 accumulators, rounded where eager bf16 ops round
+// (FastVideo fasth3_omniref_b200 README, "What --lossless-accel turns on"):
+// g and u each to bf16, silu(g) = g / (1 + e^-g) in fp32 then to bf16, and
+// the product of the two bf16 values (exact in fp32) rounded once.
+__device__ __forceinline__ uint16_t swiglu_bf16(float acc_g, float acc_u) {
+  const float g = (float)(__bf16)acc_g;
+  const float u = (float)(__bf16)acc_u;
+  const float sl = (float)(__bf16)(g / (1.0f + expf(-g)));
+  const __bf16 h = (__bf16)(sl * u);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// GATED: the MLP gate/up pair in one pass. The same X tile feeds two weights
+// (q, s = gate; q2, s2 = up) into two accumulator sets and the epilogue
+// writes swiglu(gate, up) instead of either product.
+template <int BM, int BN, int MINB, bool GATED = false>
 __global__ __launch_bounds__(kThreads, MINB)
 void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                        const float* __restrict__ s, uint16_t* __restrict__ y,
                        float* __restrict__ part, int M, int N, int K, int gk,
-                       int tiles_m, int tiles_n, int kt_per_split) {
+                       int tiles_m, int tiles_n, int kt_per_split,
+                       const uint8_t* __restrict__ q2 = nullptr,
+                       const float* __restrict__ s2 = nullptr) {
   constexpr int WN = BN / 4;            // weight rows per wave
   constexpr int NB = WN / 32;           // 32-wide MFMA column blocks per wave
   constexpr int MB = BM / 32;           // 32-tall MFMA row blocks
@@ -123,6 +140,8 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   // block, k chunk (lane / 32) of each 32-wide k slab.
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(q + (size_t)n0 * K, (uint32_t)(max(min(N - n0, BN), 0) * K));
+  const __amdgpu_buffer_rsrc_t wrs2 =
+      make_rsrc((GATED ? q2 : q) + (size_t)n0 * K, (uint32_t)(max(min(N - n0, BN), 0) * K));
   const int wkoff = (lane >> 5) * 16;
   const uint32_t woff0 = (uint32_t)((wave * WN + (lane & 31)) * K + wkoff);
   const uint32_t wnb_stride = (uint32_t)(32 * K);
@@ -142,20 +161,20 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     for (int i = 0; i < XCH; ++i)
       *reinterpret_cast<u32x4*>(&xs[buf][xs_offset(xr0 + 32 * i, xc)]) = xreg[i];
   };
-  auto load_w = [&](u32x4 (&wr)[NB][2], int kt) {
+  auto load_w = [&](u32x4 (&wr)[NB][2], int kt, __amdgpu_buffer_rsrc_t r) {
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       const bool kin = kt < kt1 && kt * kBK + sl * 32 + wkoff < K;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        wr[nb][sl] = buf_load16(wrs, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
-                                         : kOob);
+        wr[nb][sl] = buf_load16(r, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
+                                       : kOob);
     }
   };
-  auto scale_of = [&](int kt) -> float {
+  auto scale_of = [&](int kt, const float* sp) -> float {
     // always a valid address (clamped block column), zero for dead waves
     const int kb = min((kt * kBK) / kBlock, gk - 1);
-    const float v = s[(wave_live ? srow : 0) * gk + kb];
+    const float v = sp[(wave_live ? srow : 0) * gk + kb];
     return wave_live ? v : 0.0f;
   };
   // Dequantize the k16 step t of a code set into B operands.
@@ -165,15 +184,25 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
       wb[nb][t] = dequant8(wr[nb][t >> 1][(t & 1) * 2], wr[nb][t >> 1][(t & 1) * 2 + 1], sc);
   };
 
+  constexpr int MB2 = GATED ? MB : 1, NB2 = GATED ? NB : 1;
   f32x16 acc[MB][NB];
+  f32x16 acc2[MB2][NB2];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if constexpr (GATED) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
+  }
 
-  auto mfma_step = [&](int cur, bf16x8 (&wb)[NB][4]) {
+  auto mfma_step = [&](int cur, bf16x8 (&wb)[NB][4], bf16x8 (&wb2)[NB2][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int chunk = (t >> 1) * 4 + (lane >> 5) * 2 + (t & 1);
@@ -184,35 +213,45 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb[nb][t], acc[mb][nb], 0, 0, 0);
+          if constexpr (GATED)
+            acc2[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb2[nb][t], acc2[mb][nb], 0, 0, 0);
+        }
     }
   };
 
   {
     // Decode this step's codes, prefetch the next step, then the MFMAs;
     // the other resident workgroup's waves cover the decode.
-    u32x4 wr[NB][2];
-    bf16x8 wb[NB][4];
+    u32x4 wr[NB][2], wr2[NB2][2];
+    bf16x8 wb[NB][4], wb2[NB2][4];
     if (kt0 < kt1) {
       load_x(kt0);
-      load_w(wr, kt0);
+      load_w(wr, kt0, wrs);
+      if constexpr (GATED) load_w(wr2, kt0, wrs2);
       store_x(0);
     }
     __syncthreads();
     for (int kt = kt0; kt < kt1; ++kt) {
       const int cur = (kt - kt0) & 1;
-      const float sc = scale_of(kt);
+      const float sc = scale_of(kt, s);
 #pragma unroll
       for (int t = 0; t < 4; ++t) decode_t(wb, wr, sc, t);
+      if constexpr (GATED) {
+        const float sc2 = scale_of(kt, s2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) decode_t(wb2, wr2, sc2, t);
+      }
       // Branch-free step (one basic block for the scheduler): past the last
       // step these loads read zero and the staged tile goes unused.
       load_x(kt + 1);
-      load_w(wr, kt + 1);
+      load_w(wr, kt + 1, wrs);
+      if constexpr (GATED) load_w(wr2, kt + 1, wrs2);
       // Raise this wave's issue priority while it feeds the matrix core, so
       // the other workgroup's decode fills VALU slots around it.
       __builtin_amdgcn_s_setprio(1);
-      mfma_step(cur, wb);
+      mfma_step(cur, wb, wb2);
       __builtin_amdgcn_s_setprio(0);
       store_x(cur ^ 1);
       __syncthreads();
@@ -234,8 +273,12 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
         for (int r = 0; r < 16; ++r) {
           const int row = row_base + mb * 32 + (r >> 2) * 8 + (r & 3);
           if (row < M) {
-            const __bf16 v = (__bf16)acc[mb][nb][r];
-            y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, v);
+            if constexpr (GATED) {
+              y[(size_t)row * N + col] = swiglu_bf16(acc[mb][nb][r], acc2[mb][nb][r]);
+            } else {
+              const __bf16 v = (__bf16)acc[mb][nb][r];
+              y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, v);
+            }
           }
         }
       }
@@ -332,6 +375,21 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_reduce_partials(part, y, p.splits, m, n, stream);
+}
+
+// Gate/up pair: tiles as for a plain linear of the same shape, never split
+// (both accumulator sets live in registers to the end).
+hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
+                              const uint8_t* qu, const float* su, uint16_t* h,
+                              int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const int gk = (int)((k + kBlock - 1) / kBlock);
+  const int nkt = (int)((k + kBK - 1) / kBK);
+  const int tiles_m = (int)((m + 127) / 128);
+  const int tiles_n = (int)((n + 127) / 128);
+  hipLaunchKernelGGL((gemm_tiled_kernel<128, 128, 2, true>), dim3((uint32_t)(tiles_m * tiles_n), 1),
+                     dim3(kThreads), 0, stream, x, qg, sg, h, (float*)nullptr, (int)m, (int)n,
+                     (int)k, gk, tiles_m, tiles_n, nkt, qu, su);
+  return hipGetLastError();
 }
 
 }  // namespace fp8bl

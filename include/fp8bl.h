@@ -112,6 +112,23 @@ int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_
                         void* workspace, size_t workspace_bytes, int path,
                         hipStream_t stream);
 
+/* The MLP gate/up pair in one launch, with the SwiGLU epilogue (the step
+ * after the gate and up linears; FastVideo fasth3_omniref_b200 README, "What
+ * --lossless-accel turns on": SwiGLU rounds to bf16 where the eager ops do):
+ *   g = bf16_rne(x Wg_hat^T),  u = bf16_rne(x Wu_hat^T)   (as fp8_block_linear)
+ *   h = bf16_rne( bf16_rne(fl32(silu(g))) * u ),  silu(g) = g / (1 + e^-g)
+ * Both weights share the shape [n,k] and the input x; g and u never reach
+ * memory. silu is evaluated in fp32 (a few ulp), so h is graded against the
+ * exact silu(G*) U* with a bound, not bit for bit.
+ *   x                   [m,k] bf16 bits (in, 16-B aligned)
+ *   q_gate, q_up        [n,k] E4M3 bytes (in, 16-B aligned)
+ *   scale_inv_gate, scale_inv_up  [ceil(n/128),ceil(k/128)] fp32 (in, 4-B aligned)
+ *   h                   [m,n] bf16 bits (out, 16-B aligned, may not overlap)
+ * No workspace. K may be at most 2^20. */
+int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate, const float* scale_inv_gate,
+                          const uint8_t* q_up, const float* scale_inv_up, uint16_t* h,
+                          int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
 /* The converter's quantization (FastVideo PR #1829, "Changes", converter
  * bullet: E4M3 weight plus per-128x128 weight_scale_inv). For each block:
  *   amax = max |w| over the elements present in the block,

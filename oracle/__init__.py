@@ -48,4 +48,7 @@ from .fp8_block_ref import (  # noqa: F401
     gemm_bound_ratio,
     linear_bf16,
     swiglu_bf16,
+    SILU_SLOPE_MAX,
+    silu_exact,
+    swiglu_bound_ratio,
 )

@@ -307,3 +307,46 @@ def swiglu_bf16(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
         silu = g / (1.0 + np.exp(-g))
     silu_b = bf16_bits_to_f32(bf16_rne_bits(silu.astype(np.float32)))
     return bf16_rne_bits(silu_b * u)
+
+
+# ---------------------------------------------------------------------------
+# Gate/up pair with the SwiGLU epilogue (one launch on the GPU). Target:
+# h* = silu(G*) U* in fp64 from the exact gate and up products. The GPU's h
+# differs from it by the two GEMM errors carried through SwiGLU plus two bf16
+# roundings; the bound below adds them up.
+# ---------------------------------------------------------------------------
+
+SILU_SLOPE_MAX = 1.1  # max |d silu / dx| = 1.0998... (at x ~ 2.3994)
+
+
+def silu_exact(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g / (1 + e^-g) in fp64 (0 for g -> -inf)."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_bound_ratio(h_bits: np.ndarray, g_ref: np.ndarray, a_g: np.ndarray,
+                       u_ref: np.ndarray, a_u: np.ndarray) -> np.ndarray:
+    """|h - silu(G*) U*| / tol, elementwise; <= 1 passes.
+
+    With each GEMM error E = 2^-7 |Y*| + 1e-4 A (the linear's bound) and
+    s = |silu(G*)| + 1.1 E_g, v = |U*| + E_u:
+      tol = 1.1 E_g v + s E_u + 2^-6 s v
+    The first two terms carry the gate and up errors through silu (slope at
+    most 1.1) and the product; 2^-6 s v covers bf16 rounding of silu (one ulp,
+    2^-7 relative, allowing the fp32 evaluation to land on the other side of
+    a tie) and of the product (half an ulp), with room to spare. A NaN or
+    infinite h gives inf; where tol is zero, h must be zero.
+    """
+    h = bf16_bits_to_f32(h_bits).astype(np.float64)
+    e_g = 2.0 ** -7 * np.abs(g_ref) + 1e-4 * a_g
+    e_u = 2.0 ** -7 * np.abs(u_ref) + 1e-4 * a_u
+    s = np.abs(silu_exact(g_ref)) + SILU_SLOPE_MAX * e_g
+    v = np.abs(u_ref) + e_u
+    tol = SILU_SLOPE_MAX * e_g * v + s * e_u + 2.0 ** -6 * s * v
+    err = np.abs(h - silu_exact(g_ref) * u_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0),
+                         np.where(err == 0, 0.0, np.inf))
+    return np.where(np.isfinite(h), ratio, np.inf)

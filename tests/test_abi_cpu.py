@@ -20,6 +20,7 @@ def test_header_symbols_exported(lib):
         "fp8_block_abi_version", "fp8_block_status_string", "fp8_block_device_supported",
         "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
         "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
+        "fp8_block_mlp_gate_up",
     }
     for name in names:
         assert hasattr(lib, name), name
@@ -73,6 +74,24 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced here
 def test_linear_argument_errors(lib, args, status):
     x, q, s, y, m, n, k, ws, wsb, path = args
     assert L.linear_raw(x, q, s, y, m, n, k, ws, wsb, path) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (x, qg, sg, qu, su, h, m, n, k)
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 8 * FAKE, 4, 8, 15), L.FP8BL_INVALID_ARG),
+    ((FAKE, 2 * FAKE, 3 * FAKE, 0, 5 * FAKE, 8 * FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),       # null q_up
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 0, 8 * FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),       # null s_up
+    ((FAKE, 0, 3 * FAKE, 4 * FAKE, 5 * FAKE, 8 * FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),       # null q_gate
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE + 8, 5 * FAKE, 8 * FAKE, 4, 8, 16), L.FP8BL_ALIGNMENT),
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE + 2, 8 * FAKE, 4, 8, 16), L.FP8BL_ALIGNMENT),
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 4 * FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),  # h over q_up
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 5 * FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),  # h over s_up
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 8 * FAKE, 1, 8, (1 << 20) + 16), L.FP8BL_INVALID_ARG),
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 8 * FAKE, 0, 8, 16), L.FP8BL_OK),          # empty
+    ((0, 0, 0, 0, 0, 0, 4, 0, 16), L.FP8BL_OK),                                               # empty N
+])
+def test_mlp_gate_up_argument_errors(lib, args, status):
+    assert L.mlp_gate_up_raw(*args) == status
 
 
 def test_linear_workspace_errors(lib):

@@ -478,3 +478,83 @@ def test_swiglu_against_torch_and_closed_form():
     assert np.array_equal(h, ref)
     # silu(0) = 0
     assert O.swiglu_bf16(np.array([0], np.uint16), np.array([0x3F80], np.uint16))[0] == 0
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU target and bound (gate/up pair in one launch)
+# ---------------------------------------------------------------------------
+
+def test_silu_exact_closed_forms_and_torch():
+    torch = pytest.importorskip("torch")
+    x = np.linspace(-40.0, 40.0, 8001)
+    s = O.silu_exact(x)
+    # silu(x) - silu(-x) = x, silu(0) = 0, silu(x) -> x and -> 0 in the tails
+    assert np.allclose(s - O.silu_exact(-x), x, rtol=0, atol=1e-12)
+    assert O.silu_exact(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu_exact(np.array([40.0]))[0] - 40.0) < 1e-15 * 40 + 40 * np.exp(-40)
+    assert O.silu_exact(np.array([-1e4]))[0] == 0.0
+    assert np.allclose(s, torch.nn.functional.silu(torch.from_numpy(x)).numpy(), rtol=1e-15, atol=0)
+
+
+def test_silu_slope_bound():
+    # d silu / dx = sig(x) (1 + x (1 - sig(x))) in closed form; its maximum is
+    # about 1.0998 and its minimum about -0.0998, so 1.1 bounds |slope|.
+    x = np.linspace(-30.0, 30.0, 600001)
+    sig = 1.0 / (1.0 + np.exp(-x))
+    d = sig * (1.0 + x * (1.0 - sig))
+    assert np.abs(d).max() < O.SILU_SLOPE_MAX
+    assert np.abs(d).max() > 1.09
+    # and the secant slope never exceeds it either
+    sl = np.abs(np.diff(O.silu_exact(x)) / np.diff(x))
+    assert sl.max() < O.SILU_SLOPE_MAX
+
+
+def _mlp_case(seed=5, m=48, n=96, k=512):
+    rng = np.random.default_rng(seed)
+    x = O.bf16_rne_bits(rng.standard_normal((m, k)).astype(np.float32))
+    wg = O.bf16_rne_bits((rng.standard_normal((n, k)) * 0.05).astype(np.float32))
+    wu = O.bf16_rne_bits((rng.standard_normal((n, k)) * 0.05).astype(np.float32))
+    g, ag = O.linear_exact(x, wg)
+    u, au = O.linear_exact(x, wu)
+    # An fp32-accumulating emulation of the GPU side: fp32 matmul, bf16
+    # outputs, then SwiGLU with the eager rounding points.
+    xf = O.bf16_bits_to_f32(x)
+    g32 = xf @ O.bf16_bits_to_f32(wg).T
+    u32 = xf @ O.bf16_bits_to_f32(wu).T
+    h = O.swiglu_bf16(O.bf16_rne_bits(g32.astype(np.float32)),
+                      O.bf16_rne_bits(u32.astype(np.float32)))
+    return x, wg, wu, g, ag, u, au, g32, u32, h
+
+
+def test_swiglu_bound_accepts_fp32_emulation():
+    *_, g, ag, u, au, g32, u32, h = _mlp_case()
+    r = O.swiglu_bound_ratio(h, g, ag, u, au)
+    assert r.max() <= 1.0
+    # the bound is not vacuous: typical elements use a small part of it
+    assert np.median(r) < 0.5
+
+
+def test_swiglu_bound_rejects_planted_mistakes():
+    *_, g, ag, u, au, g32, u32, h = _mlp_case()
+    bf = lambda a: O.bf16_rne_bits(np.asarray(a, np.float32))  # noqa: E731
+    gb, ub = bf(g32), bf(u32)
+    wrong = {
+        "gate and up swapped": O.swiglu_bf16(ub, gb),
+        "silu dropped": bf(O.bf16_bits_to_f32(gb) * O.bf16_bits_to_f32(ub)),
+        "sign flipped": bf(-O.bf16_bits_to_f32(h)),
+        "sigmoid instead of silu": bf(1.0 / (1.0 + np.exp(-O.bf16_bits_to_f32(gb).astype(np.float64)))
+                                      * O.bf16_bits_to_f32(ub)),
+        "transposed output": h.T.copy() if h.shape[0] == h.shape[1] else h[:, ::-1].copy(),
+    }
+    for name, hb in wrong.items():
+        assert O.swiglu_bound_ratio(hb, g, ag, u, au).max() > 1.0, name
+
+
+def test_swiglu_bound_special_values():
+    z = np.zeros((2, 2))
+    zero = np.zeros((2, 2), np.uint16)
+    assert O.swiglu_bound_ratio(zero, z, z, z, z).max() == 0.0
+    one = np.full((2, 2), 0x3F80, np.uint16)
+    assert O.swiglu_bound_ratio(one, z, z, z, z).max() == np.inf
+    nan = np.full((2, 2), 0x7FC0, np.uint16)
+    assert O.swiglu_bound_ratio(nan, z + 1, z + 1, z + 1, z + 1).max() == np.inf
