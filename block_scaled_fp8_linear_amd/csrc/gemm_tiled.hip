@@ -86,14 +86,13 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float acc_g, float acc_u) {
 // GATED: the MLP gate/up pair in one pass. The same X tile feeds two weights
 // (q, s = gate; q2, s2 = up) into two accumulator sets and the epilogue
 // writes swiglu(gate, up) instead of either product.
-template <int BM, int BN, int MINB, bool GATED = false>
-__global__ __launch_bounds__(kThreads, MINB)
-void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
-                       const float* __restrict__ s, uint16_t* __restrict__ y,
-                       float* __restrict__ part, int M, int N, int K, int gk,
-                       int tiles_m, int tiles_n, int kt_per_split,
-                       const uint8_t* __restrict__ q2 = nullptr,
-                       const float* __restrict__ s2 = nullptr) {
+template <int BM, int BN, bool GATED>
+__device__ __forceinline__
+void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                const float* __restrict__ s, uint16_t* __restrict__ y,
+                float* __restrict__ part, int M, int N, int K, int gk,
+                int tiles_m, int tiles_n, int kt_per_split,
+                const uint8_t* __restrict__ q2, const float* __restrict__ s2) {
   constexpr int WN = BN / 4;            // weight rows per wave
   constexpr int NB = WN / 32;           // 32-wide MFMA column blocks per wave
   constexpr int MB = BM / 32;           // 32-tall MFMA row blocks
@@ -161,20 +160,36 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     for (int i = 0; i < XCH; ++i)
       *reinterpret_cast<u32x4*>(&xs[buf][xs_offset(xr0 + 32 * i, xc)]) = xreg[i];
   };
-  auto load_w = [&](u32x4 (&wr)[NB][2], int kt, __amdgpu_buffer_rsrc_t r) {
+  auto load_w = [&](u32x4 (&wr)[NB][2], int kt) {
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       const bool kin = kt < kt1 && kt * kBK + sl * 32 + wkoff < K;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        wr[nb][sl] = buf_load16(r, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
-                                       : kOob);
+        wr[nb][sl] = buf_load16(wrs, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
+                                         : kOob);
     }
   };
-  auto scale_of = [&](int kt, const float* sp) -> float {
+  auto scale_of = [&](int kt) -> float {
     // always a valid address (clamped block column), zero for dead waves
     const int kb = min((kt * kBK) / kBlock, gk - 1);
-    const float v = sp[(wave_live ? srow : 0) * gk + kb];
+    const float v = s[(wave_live ? srow : 0) * gk + kb];
+    return wave_live ? v : 0.0f;
+  };
+  // The same two for the second (up) weight of a gated tile.
+  auto load_w2 = [&](u32x4 (&wr)[NB][2], int kt) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const bool kin = kt < kt1 && kt * kBK + sl * 32 + wkoff < K;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        wr[nb][sl] = buf_load16(wrs2, kin ? woff0 + nb * wnb_stride + (uint32_t)(kt * kBK + sl * 32)
+                                          : kOob);
+    }
+  };
+  auto scale2_of = [&](int kt) -> float {
+    const int kb = min((kt * kBK) / kBlock, gk - 1);
+    const float v = s2[(wave_live ? srow : 0) * gk + kb];
     return wave_live ? v : 0.0f;
   };
   // Dequantize the k16 step t of a code set into B operands.
@@ -202,7 +217,23 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
         for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
   }
 
-  auto mfma_step = [&](int cur, bf16x8 (&wb)[NB][4], bf16x8 (&wb2)[NB2][4]) {
+  auto mfma_step = [&](int cur, bf16x8 (&wb)[NB][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int chunk = (t >> 1) * 4 + (lane >> 5) * 2 + (t & 1);
+      bf16x8 a[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(&xs[cur][xs_offset(mb * 32 + (lane & 31), chunk)]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb[nb][t], acc[mb][nb], 0, 0, 0);
+    }
+  };
+  // Gated step: each X fragment read from LDS feeds both weights.
+  auto mfma_step2 = [&](int cur, bf16x8 (&wb)[NB][4], bf16x8 (&wb2)[NB2][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int chunk = (t >> 1) * 4 + (lane >> 5) * 2 + (t & 1);
@@ -215,8 +246,7 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb[nb][t], acc[mb][nb], 0, 0, 0);
-          if constexpr (GATED)
-            acc2[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb2[nb][t], acc2[mb][nb], 0, 0, 0);
+          acc2[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb2[nb][t], acc2[mb][nb], 0, 0, 0);
         }
     }
   };
@@ -228,30 +258,33 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     bf16x8 wb[NB][4], wb2[NB2][4];
     if (kt0 < kt1) {
       load_x(kt0);
-      load_w(wr, kt0, wrs);
-      if constexpr (GATED) load_w(wr2, kt0, wrs2);
+      load_w(wr, kt0);
+      if constexpr (GATED) load_w2(wr2, kt0);
       store_x(0);
     }
     __syncthreads();
     for (int kt = kt0; kt < kt1; ++kt) {
       const int cur = (kt - kt0) & 1;
-      const float sc = scale_of(kt, s);
+      const float sc = scale_of(kt);
 #pragma unroll
       for (int t = 0; t < 4; ++t) decode_t(wb, wr, sc, t);
       if constexpr (GATED) {
-        const float sc2 = scale_of(kt, s2);
+        const float sc2 = scale2_of(kt);
 #pragma unroll
         for (int t = 0; t < 4; ++t) decode_t(wb2, wr2, sc2, t);
       }
       // Branch-free step (one basic block for the scheduler): past the last
       // step these loads read zero and the staged tile goes unused.
       load_x(kt + 1);
-      load_w(wr, kt + 1, wrs);
-      if constexpr (GATED) load_w(wr2, kt + 1, wrs2);
+      load_w(wr, kt + 1);
+      if constexpr (GATED) load_w2(wr2, kt + 1);
       // Raise this wave's issue priority while it feeds the matrix core, so
       // the other workgroup's decode fills VALU slots around it.
       __builtin_amdgcn_s_setprio(1);
-      mfma_step(cur, wb, wb2);
+      if constexpr (GATED)
+        mfma_step2(cur, wb, wb2);
+      else
+        mfma_step(cur, wb);
       __builtin_amdgcn_s_setprio(0);
       store_x(cur ^ 1);
       __syncthreads();
@@ -301,6 +334,26 @@ void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   }
 }
 
+template <int BM, int BN, int MINB>
+__global__ __launch_bounds__(kThreads, MINB)
+void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                       const float* __restrict__ s, uint16_t* __restrict__ y,
+                       float* __restrict__ part, int M, int N, int K, int gk,
+                       int tiles_m, int tiles_n, int kt_per_split) {
+  tiled_body<BM, BN, false>(x, q, s, y, part, M, N, K, gk, tiles_m, tiles_n, kt_per_split,
+                            nullptr, nullptr);
+}
+
+template <int BM, int BN, int MINB>
+__global__ __launch_bounds__(kThreads, MINB)
+void gemm_gated_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qg,
+                       const float* __restrict__ sg, const uint8_t* __restrict__ qu,
+                       const float* __restrict__ su, uint16_t* __restrict__ h, int M, int N,
+                       int K, int gk, int tiles_m, int tiles_n) {
+  tiled_body<BM, BN, true>(x, qg, sg, h, nullptr, M, N, K, gk, tiles_m, tiles_n,
+                           (K + kBK - 1) / kBK, qu, su);
+}
+
 struct TiledPlan {
   int cfg;          // 0: 128x256, 1: 256x128, 2: 128x128 (all 2 workgroups per CU)
   int bm, bn, splits, kt_per_split;
@@ -325,14 +378,28 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
     }
   }
   const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + p.bn - 1) / p.bn);
-  // Fewer tiles than CUs: split K until there are >= 512 work items (2
-  // workgroups per CU), keeping >= 8 K steps per split. Measured on the
-  // M=512 text-encoder shapes: 160 tiles of 128x128 run best as 4 splits,
-  // while 400 tiles of 256x128 run best unsplit (the partials' round trip
-  // costs more than the idle slots).
+  // Fewer tiles than CUs: split K. The split count minimises a cost model:
+  // the busiest CU runs ceil(W / 256) of the W workgroups (one alone runs
+  // at ~60% of a pair's rate), each for ceil(nkt / s) steps, and the fp32
+  // partials cost 4 bytes per output and split to write and read back, plus
+  // 2 bytes of bf16 output, at ~5 TB/s. Measured on the M=512 text-encoder
+  // shapes (160 tiles of 128x128): 3 splits (480 workgroups, at most two per
+  // CU) beat 4 (640, up to three per CU). 400 tiles of 256x128 run best
+  // unsplit (the partials' round trip costs more than the idle slots).
   int splits = 1;
-  if (tiles < 256)
-    while (tiles * splits < 512 && splits < 8 && nkt / (splits * 2) >= 8) splits *= 2;
+  if (tiles < 256) {
+    const double kStepUs = 0.75;              // one 128x128 step, two workgroups per CU
+    double best = 1e30;
+    for (int sp = 1; sp <= 8; ++sp) {
+      const int steps = (nkt + sp - 1) / sp;
+      if (sp > 1 && steps < 8) break;
+      const int64_t w = tiles * sp;
+      const double load = w <= 256 ? 1.67 : (double)((w + 255) / 256);
+      double cost = load * steps * kStepUs;
+      if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
+      if (cost < best) { best = cost; splits = sp; }
+    }
+  }
   p.kt_per_split = (nkt + splits - 1) / splits;
   p.splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
   return p;
@@ -383,12 +450,11 @@ hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float*
                               const uint8_t* qu, const float* su, uint16_t* h,
                               int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const int gk = (int)((k + kBlock - 1) / kBlock);
-  const int nkt = (int)((k + kBK - 1) / kBK);
   const int tiles_m = (int)((m + 127) / 128);
   const int tiles_n = (int)((n + 127) / 128);
-  hipLaunchKernelGGL((gemm_tiled_kernel<128, 128, 2, true>), dim3((uint32_t)(tiles_m * tiles_n), 1),
-                     dim3(kThreads), 0, stream, x, qg, sg, h, (float*)nullptr, (int)m, (int)n,
-                     (int)k, gk, tiles_m, tiles_n, nkt, qu, su);
+  hipLaunchKernelGGL((gemm_gated_kernel<128, 128, 2>), dim3((uint32_t)(tiles_m * tiles_n), 1),
+                     dim3(kThreads), 0, stream, x, qg, sg, qu, su, h, (int)m, (int)n, (int)k, gk,
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 
