@@ -17,6 +17,9 @@ Sources (page titles and sections, not line numbers):
     - "Changes", tests bullet: the dequantizer is bit-exact against the
       reference broadcast, and the FP8 round trip stays within E4M3 precision.
 * LightX2V PR #1657, "Walkthrough": FP8 GEMM with FP32 accumulation.
+* FastVideo PR #1829, "Changes", first bullet: the Blackwell route also
+  needs a Triton quantizer beside the FlashInfer groupwise GEMM; read here as
+  per-token 1x128 activation quantization for a W8A8 product.
 * FastVideo ``fasth3_omniref_b200`` README, "What --lossless-accel turns on":
   bf16 rounding happens at the same points as the eager ops.
 
@@ -51,4 +54,9 @@ from .fp8_block_ref import (  # noqa: F401
     SILU_SLOPE_MAX,
     silu_exact,
     swiglu_bound_ratio,
+    act_quantize,
+    act_dequant_f64,
+    weight_dequant_f64,
+    linear_w8a8_exact,
+    linear_w8a8_sampled,
 )

@@ -350,3 +350,82 @@ def swiglu_bound_ratio(h_bits: np.ndarray, g_ref: np.ndarray, a_g: np.ndarray,
         ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0),
                          np.where(err == 0, 0.0, np.inf))
     return np.where(np.isfinite(h), ratio, np.inf)
+
+
+# ---------------------------------------------------------------------------
+# W8A8 variant (both operands E4M3). FastVideo PR #1829, "Changes", first
+# bullet: on Blackwell the loader also needs a Triton quantizer next to the
+# FlashInfer groupwise GEMM. The pages do not say what that quantizer does;
+# the reading taken here is per-token activation quantization in 1x128
+# groups along K, with the weight's own arithmetic (S = fl32(amax / 448),
+# 1.0 for an all-zero group, nearest finite E4M3 of fl32(x / S)), and a GEMM
+# that multiplies E4M3 codes exactly and applies x_scale * w_scale to the
+# sum of each 128-wide K block. Activation scales are stored K-block-major,
+# x_scale[GK, M], so that one K block's scales for consecutive rows are
+# contiguous.
+# ---------------------------------------------------------------------------
+
+def act_quantize(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 X bits [M,K] -> (XQ uint8 [M,K], x_scale fp32 [GK, M]).
+
+    Every 1x128 group of a row (the last one may be shorter) gets its own
+    scale S = fl32(amax / 448) (1.0 if the group is all zero) and codes
+    e4m3_nearest(fl32(x / S)). X must be finite."""
+    x = bf16_bits_to_f32(np.asarray(x_bits))
+    if not np.all(np.isfinite(x)):
+        raise ValueError("activation must be finite")
+    m, k = x.shape
+    gk = (k + BLOCK - 1) // BLOCK
+    xq = np.empty((m, k), dtype=np.uint8)
+    xs = np.empty((gk, m), dtype=np.float32)
+    for j in range(gk):
+        cs = slice(j * BLOCK, min((j + 1) * BLOCK, k))
+        grp = x[:, cs]                                          # [M, <=128]
+        amax = np.max(np.abs(grp), axis=1).astype(np.float32)   # per row
+        sc = np.where(amax == 0, np.float32(1.0),
+                      (amax / np.float32(E4M3_MAX)).astype(np.float32)).astype(np.float32)
+        xs[j] = sc
+        xq[:, cs] = e4m3_encode_nearest((grp / sc[:, None]).astype(np.float32))
+    return xq, xs
+
+
+def act_dequant_f64(xq: np.ndarray, x_scale: np.ndarray) -> np.ndarray:
+    """XQ [M,K] and x_scale [GK,M] -> the exact values e4m3(XQ) * S in fp64."""
+    m, k = xq.shape
+    t = e4m3_table()[xq]
+    s = np.repeat(np.asarray(x_scale, np.float64).T, BLOCK, axis=1)[:, :k]
+    return t * s
+
+
+def weight_dequant_f64(q: np.ndarray, scale_inv: np.ndarray) -> np.ndarray:
+    """Q [N,K] and S [GN,GK] -> the exact values e4m3(Q) * S in fp64 (no bf16
+    rounding: in the W8A8 product the codes meet the scales only after the
+    exact per-block sums)."""
+    n, k = q.shape
+    return e4m3_table()[q] * _expand_scales(scale_inv, n, k).astype(np.float64)
+
+
+def linear_w8a8_exact(xq: np.ndarray, x_scale: np.ndarray, q: np.ndarray,
+                      scale_inv: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Y*[m,n] = sum_kb x_scale[kb,m] S[n/128,kb] sum_{k in kb} e4m3(XQ[m,k]) e4m3(Q[n,k])
+    in fp64, and A = the same sum over absolute values."""
+    xv = act_dequant_f64(xq, x_scale)
+    wv = weight_dequant_f64(q, scale_inv)
+    return xv @ wv.T, np.abs(xv) @ np.abs(wv).T
+
+
+def linear_w8a8_sampled(xq: np.ndarray, x_scale: np.ndarray, q: np.ndarray,
+                        scale_inv: np.ndarray, ms: np.ndarray, ns: np.ndarray
+                        ) -> tuple[np.ndarray, np.ndarray]:
+    """Y*[ms[i], ns[i]] and A[ms[i], ns[i]] one output at a time (fp64)."""
+    ms = np.asarray(ms, dtype=np.int64)
+    ns = np.asarray(ns, dtype=np.int64)
+    n, k = q.shape
+    gk = (k + BLOCK - 1) // BLOCK
+    xv = e4m3_table()[np.asarray(xq)[ms]] * np.repeat(
+        np.asarray(x_scale, np.float64)[:, ms].T, BLOCK, axis=1)[:, :k]
+    wrows = np.asarray(q)[ns]
+    srows = np.asarray(scale_inv, np.float64)[ns // BLOCK]           # [P, GK]
+    wv = e4m3_table()[wrows] * np.repeat(srows, BLOCK, axis=1)[:, :k]
+    assert srows.shape[1] == gk
+    return np.einsum("pk,pk->p", xv, wv), np.einsum("pk,pk->p", np.abs(xv), np.abs(wv))

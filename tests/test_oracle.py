@@ -558,3 +558,108 @@ def test_swiglu_bound_special_values():
     assert O.swiglu_bound_ratio(one, z, z, z, z).max() == np.inf
     nan = np.full((2, 2), 0x7FC0, np.uint16)
     assert O.swiglu_bound_ratio(nan, z + 1, z + 1, z + 1, z + 1).max() == np.inf
+
+
+# ---------------------------------------------------------------------------
+# W8A8 variant: activation quantizer and the exact block-scaled product
+# ---------------------------------------------------------------------------
+
+def _bf16_rows(seed, m, k, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return O.bf16_rne_bits((rng.standard_normal((m, k)) * scale).astype(np.float32))
+
+
+def test_act_quantize_equals_weight_quantizer_per_row():
+    # A [1,K] matrix's 128x128 blocks are exactly the 1x128 groups of that
+    # row, so the (separately pinned) weight quantizer fixes every row.
+    x = _bf16_rows(21, 9, 400, 3.0)
+    x[2, 128:256] = 0                       # an all-zero group -> scale 1, codes 0
+    x[4, :5] = 0x0001                       # subnormal bf16 values in a group
+    xq, xs = O.act_quantize(x)
+    assert xq.shape == (9, 400) and xs.shape == (4, 9)
+    xf = O.bf16_bits_to_f32(x)
+    for r in range(9):
+        q, s = O.quantize(xf[r:r + 1])
+        assert np.array_equal(xq[r], q[0]), r
+        assert np.array_equal(xs[:, r], s[0]), r
+    assert xs[1, 2] == 1.0 and np.all(xq[2, 128:256] == 0)
+
+
+def test_act_quantize_group_max_hits_448_and_roundtrip():
+    x = _bf16_rows(22, 16, 1024, 0.5)
+    xq, xs = O.act_quantize(x)
+    mag = xq & 0x7F
+    for j in range(8):
+        assert np.all(mag[:, j * 128:(j + 1) * 128].max(axis=1) == 0x7E)
+    xv = O.act_dequant_f64(xq, xs)
+    xf = O.bf16_bits_to_f32(x).astype(np.float64)
+    # normal range: |err| <= 2^-4 |x| (half of the 3-bit mantissa step);
+    # subnormal range: |err| <= 2^-10 S (half the subnormal step 2^-9 S)
+    s_full = np.repeat(xs.T.astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(xv - xf) <= np.maximum(2.0 ** -4 * np.abs(xf), 2.0 ** -10 * s_full) * (1 + 1e-12))
+
+
+def test_w8a8_product_exact_rational_brute_force():
+    from fractions import Fraction
+    rng = np.random.default_rng(23)
+    m, n, k = 3, 130, 272                   # two N blocks, three K blocks (last ragged)
+    xq = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    q = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x3A          # no NaN codes
+    q[(q & 0x7F) == 0x7F] = 0x41
+    xs = rng.uniform(1e-3, 2.0, (3, m)).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-1, (2, 3)).astype(np.float32)
+    y, a = O.linear_w8a8_exact(xq, xs, q, ws)
+    tab = {c: Fraction(O.e4m3_value(c)) for c in range(256) if (c & 0x7F) != 0x7F}
+    for mi in range(m):
+        for ni in (0, 1, 127, 128, 129):
+            tot, ab = Fraction(0), Fraction(0)
+            for kb in range(3):
+                part = sum((tab[xq[mi, kk]] * tab[q[ni, kk]]
+                            for kk in range(kb * 128, min(kb * 128 + 128, k))), Fraction(0))
+                pab = sum((abs(tab[xq[mi, kk]] * tab[q[ni, kk]])
+                           for kk in range(kb * 128, min(kb * 128 + 128, k))), Fraction(0))
+                sc = Fraction(float(xs[kb, mi])) * Fraction(float(ws[ni // 128, kb]))
+                tot += sc * part
+                ab += abs(sc) * pab
+            assert abs(Fraction(y[mi, ni]) - tot) <= Fraction(1, 10 ** 12) * ab + Fraction(1, 10 ** 300)
+            assert abs(Fraction(a[mi, ni]) - ab) <= Fraction(1, 10 ** 12) * ab
+    # sampled form agrees with the full product
+    ms = np.array([0, 2, 1]); ns = np.array([129, 0, 64])
+    ys, as_ = O.linear_w8a8_sampled(xq, xs, q, ws, ms, ns)
+    assert np.allclose(ys, y[ms, ns], rtol=1e-13, atol=0) and np.allclose(as_, a[ms, ns], rtol=1e-13)
+
+
+def test_w8a8_reduces_to_w8a16_when_exact_in_bf16():
+    # With power-of-two scales every e4m3 * scale is exact in bf16 (4-bit
+    # significand), so the W8A8 target equals the W8A16 one on those values.
+    rng = np.random.default_rng(24)
+    m, n, k = 5, 140, 300
+    xq = rng.integers(0, 0x7F, (m, k)).astype(np.uint8) | (rng.integers(0, 2, (m, k)) << 7).astype(np.uint8)
+    q = rng.integers(0, 0x7F, (n, k)).astype(np.uint8)
+    xs = (2.0 ** rng.integers(-8, 3, (3, m))).astype(np.float32)
+    ws = (2.0 ** rng.integers(-12, -4, (2, 3))).astype(np.float32)
+    x_bits = O.bf16_rne_bits(O.act_dequant_f64(xq, xs).astype(np.float32))
+    assert np.array_equal(O.bf16_bits_to_f32(x_bits).astype(np.float64), O.act_dequant_f64(xq, xs))
+    y8, a8 = O.linear_w8a8_exact(xq, xs, q, ws)
+    y16, a16 = O.linear_exact(x_bits, O.dequant(q, ws))
+    assert np.allclose(y8, y16, rtol=1e-14, atol=1e-300)
+    assert np.allclose(a8, a16, rtol=1e-14, atol=1e-300)
+
+
+def test_w8a8_planted_scale_mistakes_detected():
+    rng = np.random.default_rng(25)
+    m, n, k = 4, 256, 384
+    x = _bf16_rows(26, m, k)
+    xq, xs = O.act_quantize(x)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    w[:128] *= 8.0                          # the two N blocks get different scales
+    q, ws = O.quantize(w)
+    y, a = O.linear_w8a8_exact(xq, xs, q, ws)
+    # the W8A8 target tracks the unquantized product within E4M3 error
+    ref = O.bf16_bits_to_f32(x).astype(np.float64) @ w.astype(np.float64).T
+    assert np.all(np.abs(y - ref) <= 0.15 * a)
+    wrong_x = O.linear_w8a8_exact(xq, xs[::-1].copy(), q, ws)[0]        # K blocks swapped
+    wrong_w = O.linear_w8a8_exact(xq, xs, q, ws[::-1].copy())[0]        # N blocks swapped
+    for bad in (wrong_x, wrong_w):
+        assert O.gemm_bound_ratio(O.bf16_rne_bits(bad.astype(np.float32)), y, a).max() > 1.0
