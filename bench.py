@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 MALL_BYTES = 256 << 20
 
@@ -119,10 +120,13 @@ def main():
     ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0 = auto)")
-    ap.add_argument("--op", default="linear", choices=["linear", "dequant", "quantize", "mlp"],
+    ap.add_argument("--op", default="linear",
+                    choices=["linear", "dequant", "quantize", "mlp", "w8a8", "w8a8_gemm"],
                     help="linear (default): the fused layer; dequant / quantize: the "
                          "standalone kernels on the workload's weight; mlp: the gate/up "
-                         "pair with the SwiGLU epilogue in one launch (workload mlp_gate)")
+                         "pair with the SwiGLU epilogue in one launch (workload mlp_gate); "
+                         "w8a8: per-token activation quantize + FP8 x FP8 GEMM from bf16 X; "
+                         "w8a8_gemm: the FP8 GEMM alone on pre-quantized X")
     ap.add_argument("--eager", action="store_true",
                     help="time K separate calls instead of one replay of a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -185,11 +189,15 @@ def main():
         ups = [F.fp8_block_quantize(wu_dev) for _ in range(rotate)]
         del wu_dev
     ws_bytes = F.workspace_size(m, n, k)
+    if args.op in ("w8a8", "w8a8_gemm"):
+        ws_bytes = F.w8a8_workspace_size(m, n, k)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     if args.op == "dequant":
         wouts = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
+    if args.op == "w8a8_gemm":
+        xqs = [F.fp8_act_quantize(st[0]) for st in sets]
     if args.op == "quantize":
         w_srcs = [torch.from_numpy(lin.w).to(dev) for _ in range(min(rotate, 4))]
 
@@ -197,6 +205,11 @@ def main():
         x, q, s, y = sets[i % rotate]
         if args.op == "linear":
             F.fp8_block_linear(x, q, s, out=y, workspace=ws)
+        elif args.op == "w8a8":
+            F.fp8_block_linear_w8a8_bf16(x, q, s, out=y, workspace=ws)
+        elif args.op == "w8a8_gemm":
+            xq, xs = xqs[i % rotate]
+            F.fp8_block_linear_w8a8(xq, xs, q, s, out=y, workspace=ws)
         elif args.op == "mlp":
             qu, su = ups[i % rotate]
             F.fp8_block_mlp_gate_up(x, q, s, qu, su, out=y)
@@ -252,12 +265,18 @@ def main():
     elif args.op == "mlp":            # two products over one X, one bf16 output
         flops = 4.0 * m * n * k
         abytes = 2 * m * k + 2 * (n * k + 4 * gn * gk) + 2 * m * n
+    mfma_peak, dtype = MFMA_BF16_PEAK_TFLOPS, "bf16"
+    if args.op in ("w8a8", "w8a8_gemm"):
+        # E4M3 x E4M3 products on the fp8 matrix cores, fp32 accumulation
+        mfma_peak, dtype = MFMA_FP8_PEAK_TFLOPS, "fp8_e4m3"
+        abytes = (m * k + 4 * m * -(-k // 128) + n * k + 4 * gn * gk + 2 * m * n
+                  + (3 * m * k if args.op == "w8a8" else 0))
     if bound == "hbm":
         unit, value = "GB/s", abytes * args.steps / wall / 1e9
         achieved, peak, r_unit = abytes / avg_launch_s / 1e9, HBM_PEAK_GBPS, "GB/s"
     else:
         unit, value = "TFLOP/s", flops * args.steps / wall / 1e12
-        achieved, peak, r_unit = flops / avg_launch_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved, peak, r_unit = flops / avg_launch_s / 1e12, mfma_peak, "TFLOP/s"
 
     out = {
         "metric": "FP8-block linear TFLOP/s (% bf16 MFMA peak) and weight GB/s (% HBM) at M<=32",
@@ -270,7 +289,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "op": args.op, "m": m, "n": n, "k": k,
                    "weight": "e4m3 + fp32 128x128 scale_inv", "rotated_sets": rotate,

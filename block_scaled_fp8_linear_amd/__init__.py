@@ -11,6 +11,9 @@ hand-written HIP) provides:
 * ``fp8_block_linear(x, q, s)`` -> bf16 Y = X W_hat^T, fp32 accumulation
 * ``fp8_block_mlp_gate_up(x, qg, sg, qu, su)`` -> bf16 swiglu(X Wg^T, X Wu^T)
   in one launch (the MLP's gate/up pair)
+* ``fp8_act_quantize(x)`` -> (xq, x_scale)  per-token 1x128 activation quantizer
+* ``fp8_block_linear_w8a8(xq, x_scale, q, s)`` / ``fp8_block_linear_w8a8_bf16(x, q, s)``
+  -> bf16 Y from E4M3 x E4M3 products on the FP8 matrix cores (W8A8 route)
 
 The functions here only marshal torch tensors (device memory and the current
 stream) into the C ABI declared in include/fp8bl.h; all arithmetic runs in
@@ -25,14 +28,15 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     PATH_AUTO, PATH_SKINNY, PATH_TILED, Fp8blError, abi_version, device_supported,
-    status_string, workspace_size,
+    status_string, w8a8_workspace_size, workspace_size,
 )
 
 BLOCK = 128
 
 __all__ = [
     "fp8_block_quantize", "fp8_block_dequant", "fp8_block_linear", "fp8_block_mlp_gate_up",
-    "workspace_size",
+    "fp8_act_quantize", "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16",
+    "workspace_size", "w8a8_workspace_size",
     "device_supported", "abi_version", "status_string", "Fp8blError",
     "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "scale_grid_shape",
 ]
@@ -161,4 +165,92 @@ def fp8_block_mlp_gate_up(x: torch.Tensor, q_gate: torch.Tensor, s_gate: torch.T
         _check(_lib.mlp_gate_up_raw(x.data_ptr(), q_gate.data_ptr(), s_gate.data_ptr(),
                                     q_up.data_ptr(), s_up.data_ptr(), out.data_ptr(),
                                     m, n, k, _stream(x.device)), "fp8_block_mlp_gate_up")
+    return out
+
+
+def x_scale_shape(m: int, k: int) -> tuple[int, int]:
+    """Activation scales are K-block-major: [ceil(K/128), M]."""
+    return ((k + BLOCK - 1) // BLOCK, m)
+
+
+def fp8_act_quantize(x: torch.Tensor, xq: torch.Tensor | None = None,
+                     x_scale: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 x [M,K] -> (xq uint8 [M,K], x_scale fp32 [ceil(K/128), M])."""
+    _need(x, torch.bfloat16, "x")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(x_scale_shape(m, k), dtype=torch.float32, device=x.device)
+    _need(xq, torch.uint8, "xq")
+    _need(x_scale, torch.float32, "x_scale")
+    if tuple(xq.shape) != (m, k) or tuple(x_scale.shape) != x_scale_shape(m, k):
+        raise ValueError("output shapes do not match x")
+    with torch.cuda.device(x.device):
+        _check(_lib.act_quantize_raw(x.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k,
+                                     _stream(x.device)), "fp8_act_quantize")
+    return xq, x_scale
+
+
+def _w8a8_workspace(m, n, k, workspace, dev):
+    need = w8a8_workspace_size(m, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return workspace, ws_ptr, ws_bytes
+
+
+def fp8_block_linear_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, q: torch.Tensor,
+                          s: torch.Tensor, out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3 xq [M,K] + x_scale [ceil(K/128), M], block-FP8 weight -> bf16 y [M,N]."""
+    _need(xq, torch.uint8, "xq")
+    _need(x_scale, torch.float32, "x_scale")
+    _need(q, torch.uint8, "q")
+    _need(s, torch.float32, "s")
+    m, k = xq.shape
+    n, kq = q.shape
+    if kq != k:
+        raise ValueError(f"K mismatch: xq has {k}, q has {kq}")
+    if tuple(x_scale.shape) != x_scale_shape(m, k):
+        raise ValueError(f"x_scale must be {x_scale_shape(m, k)}, got {tuple(x_scale.shape)}")
+    if tuple(s.shape) != scale_grid_shape(n, k):
+        raise ValueError(f"scale grid must be {scale_grid_shape(n, k)}, got {tuple(s.shape)}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out shape")
+    workspace, ws_ptr, ws_bytes = _w8a8_workspace(m, n, k, workspace, xq.device)
+    with torch.cuda.device(xq.device):
+        _check(_lib.linear_w8a8_raw(xq.data_ptr(), x_scale.data_ptr(), q.data_ptr(), s.data_ptr(),
+                                    out.data_ptr(), m, n, k, ws_ptr, ws_bytes,
+                                    _stream(xq.device)), "fp8_block_linear_w8a8")
+    return out
+
+
+def fp8_block_linear_w8a8_bf16(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
+                               out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 x [M,K] -> quantize per token (1x128) -> W8A8 GEMM -> bf16 y [M,N]."""
+    _need(x, torch.bfloat16, "x")
+    _need(q, torch.uint8, "q")
+    _need(s, torch.float32, "s")
+    m, k = x.shape
+    n, kq = q.shape
+    if kq != k:
+        raise ValueError(f"K mismatch: x has {k}, q has {kq}")
+    if tuple(s.shape) != scale_grid_shape(n, k):
+        raise ValueError(f"scale grid must be {scale_grid_shape(n, k)}, got {tuple(s.shape)}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out shape")
+    workspace, ws_ptr, ws_bytes = _w8a8_workspace(m, n, k, workspace, x.device)
+    with torch.cuda.device(x.device):
+        _check(_lib.linear_w8a8_bf16_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), out.data_ptr(),
+                                         m, n, k, ws_ptr, ws_bytes, _stream(x.device)),
+               "fp8_block_linear_w8a8_bf16")
     return out

@@ -61,6 +61,14 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_linear_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, c_int, vp]
     lib.fp8_block_mlp_gate_up.restype = c_int
     lib.fp8_block_mlp_gate_up.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_act_quantize.restype = c_int
+    lib.fp8_act_quantize.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.fp8_block_linear_w8a8_workspace_size.restype = sz
+    lib.fp8_block_linear_w8a8_workspace_size.argtypes = [i64, i64, i64]
+    lib.fp8_block_linear_w8a8.restype = c_int
+    lib.fp8_block_linear_w8a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    lib.fp8_block_linear_w8a8_bf16.restype = c_int
+    lib.fp8_block_linear_w8a8_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
     lib.fp8_block_quantize.restype = c_int
     lib.fp8_block_quantize.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fp8_block_quantize_bf16.restype = c_int
@@ -73,7 +81,7 @@ def header_functions() -> list[str]:
     """Names of the functions include/fp8bl.h declares."""
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp8_block_\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp8_\w+)\s*\(", text, flags=re.M)
 
 
 def status_string(status: int) -> str:
@@ -107,6 +115,24 @@ def linear_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,
 def mlp_gate_up_raw(x: int, qg: int, sg: int, qu: int, su: int, h: int,
                     m: int, n: int, k: int, stream: int = 0) -> int:
     return load().fp8_block_mlp_gate_up(x, qg, sg, qu, su, h, m, n, k, stream)
+
+
+def act_quantize_raw(x: int, xq: int, xs: int, m: int, k: int, stream: int = 0) -> int:
+    return load().fp8_act_quantize(x, xq, xs, m, k, stream)
+
+
+def w8a8_workspace_size(m: int, n: int, k: int) -> int:
+    return int(load().fp8_block_linear_w8a8_workspace_size(int(m), int(n), int(k)))
+
+
+def linear_w8a8_raw(xq: int, xs: int, q: int, s: int, y: int, m: int, n: int, k: int,
+                    ws: int, ws_bytes: int, stream: int = 0) -> int:
+    return load().fp8_block_linear_w8a8(xq, xs, q, s, y, m, n, k, ws, ws_bytes, stream)
+
+
+def linear_w8a8_bf16_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,
+                         ws: int, ws_bytes: int, stream: int = 0) -> int:
+    return load().fp8_block_linear_w8a8_bf16(x, q, s, y, m, n, k, ws, ws_bytes, stream)
 
 
 def quantize_raw(w: int, q: int, s: int, n: int, k: int, stream: int = 0) -> int:

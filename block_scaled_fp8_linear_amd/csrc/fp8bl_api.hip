@@ -80,6 +80,38 @@ int validate_linear(const uint16_t* x, const uint8_t* q, const float* s, const u
   return FP8BL_OK;
 }
 
+size_t x_scale_elems(int64_t m, int64_t k) {
+  return (size_t)((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK) * (size_t)m;
+}
+
+// Shape rules of the W8A8 GEMM (as the bf16 linear) plus the operands'
+// alignment and the output's overlap with them.
+int validate_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const float* s,
+                  const uint16_t* y, int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || m >= kMaxDim) return FP8BL_INVALID_ARG;
+  int st = check_nk(n, k);
+  if (st != FP8BL_OK) return st;
+  if (k > kMaxLinearK) return FP8BL_INVALID_ARG;
+  if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && n > 0 && m * n > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  if (!xq || !xs || !q || !s || !y) return FP8BL_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(s, 4))
+    return FP8BL_ALIGNMENT;
+  const size_t ybytes = (size_t)m * n * 2;
+  if (overlap(y, ybytes, xq, (size_t)m * k) || overlap(y, ybytes, q, (size_t)n * k) ||
+      overlap(y, ybytes, s, grid_elems(n, k) * 4) || overlap(y, ybytes, xs, x_scale_elems(m, k) * 4))
+    return FP8BL_INVALID_ARG;
+  return FP8BL_OK;
+}
+
+// Workspace of fp8_block_linear_w8a8_bf16: the quantized activation, its
+// scales, then the GEMM's split-K partials, each 256-byte aligned.
+size_t w8a8_act_bytes(int64_t m, int64_t k) {
+  return fp8bl::round_up((size_t)m * k, fp8bl::kWorkspaceAlign) +
+         fp8bl::round_up(x_scale_elems(m, k) * 4, fp8bl::kWorkspaceAlign);
+}
+
 }  // namespace
 
 FP8BL_EXPORT int fp8_block_abi_version(void) { return FP8BL_ABI_VERSION; }
@@ -175,6 +207,78 @@ FP8BL_EXPORT int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate,
   if (st != FP8BL_OK) return st;
   return hip_status(fp8bl::launch_mlp_gate_up(x, q_gate, scale_inv_gate, q_up, scale_inv_up, h,
                                               m, n, k, stream));
+}
+
+FP8BL_EXPORT int fp8_act_quantize(const uint16_t* x, uint8_t* xq, float* x_scale, int64_t m,
+                                  int64_t k, hipStream_t stream) {
+  if (m < 0 || k <= 0 || (k % 16) != 0 || m >= kMaxDim || k >= kMaxDim) return FP8BL_INVALID_ARG;
+  if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
+  if ((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK > 65535) return FP8BL_INVALID_ARG;
+  if (m == 0) return FP8BL_OK;
+  if (!x || !xq || !x_scale) return FP8BL_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4)) return FP8BL_ALIGNMENT;
+  const size_t sbytes = x_scale_elems(m, k) * 4;
+  if (overlap(xq, (size_t)m * k, x, (size_t)m * k * 2) || overlap(x_scale, sbytes, x, (size_t)m * k * 2) ||
+      overlap(xq, (size_t)m * k, x_scale, sbytes))
+    return FP8BL_INVALID_ARG;
+  int st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_act_quantize(x, xq, x_scale, m, k, stream));
+}
+
+FP8BL_EXPORT size_t fp8_block_linear_w8a8_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || (k % 16) != 0) return 0;
+  if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return 0;
+  return w8a8_act_bytes(m, k) + fp8bl::w8a8_partials_bytes(m, n, k);
+}
+
+FP8BL_EXPORT int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t* q,
+                                       const float* scale_inv, uint16_t* y, int64_t m, int64_t n,
+                                       int64_t k, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  int st = validate_w8a8(xq, x_scale, q, scale_inv, y, m, n, k);
+  if (st != FP8BL_OK) return st;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  const size_t need = fp8bl::w8a8_partials_bytes(m, n, k);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FP8BL_WORKSPACE;
+    if (!aligned(workspace, fp8bl::kWorkspaceAlign)) return FP8BL_ALIGNMENT;
+    if (overlap(workspace, need, y, (size_t)m * n * 2) || overlap(workspace, need, xq, (size_t)m * k) ||
+        overlap(workspace, need, q, (size_t)n * k) ||
+        overlap(workspace, need, scale_inv, grid_elems(n, k) * 4) ||
+        overlap(workspace, need, x_scale, x_scale_elems(m, k) * 4))
+      return FP8BL_INVALID_ARG;
+  }
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_gemm_w8a8(xq, x_scale, q, scale_inv, y, m, n, k, workspace,
+                                            workspace_bytes, stream));
+}
+
+FP8BL_EXPORT int fp8_block_linear_w8a8_bf16(const uint16_t* x, const uint8_t* q,
+                                            const float* scale_inv, uint16_t* y, int64_t m,
+                                            int64_t n, int64_t k, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  int st = validate_linear(x, q, scale_inv, y, m, n, k, FP8BL_PATH_AUTO);
+  if (st != FP8BL_OK) return st;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  const size_t need = fp8_block_linear_w8a8_workspace_size(m, n, k);
+  if (workspace == nullptr || workspace_bytes < need) return FP8BL_WORKSPACE;
+  if (!aligned(workspace, fp8bl::kWorkspaceAlign)) return FP8BL_ALIGNMENT;
+  if (overlap(workspace, need, y, (size_t)m * n * 2) || overlap(workspace, need, x, (size_t)m * k * 2) ||
+      overlap(workspace, need, q, (size_t)n * k) ||
+      overlap(workspace, need, scale_inv, grid_elems(n, k) * 4))
+    return FP8BL_INVALID_ARG;
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = ws;
+  float* xs = reinterpret_cast<float*>(ws + fp8bl::round_up((size_t)m * k, fp8bl::kWorkspaceAlign));
+  uint8_t* part = ws + w8a8_act_bytes(m, k);
+  hipError_t e = fp8bl::launch_act_quantize(x, xq, xs, m, k, stream);
+  if (e != hipSuccess) return FP8BL_HIP_ERROR;
+  return hip_status(fp8bl::launch_gemm_w8a8(xq, xs, q, scale_inv, y, m, n, k, part,
+                                            need - w8a8_act_bytes(m, k), stream));
 }
 
 FP8BL_EXPORT int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,

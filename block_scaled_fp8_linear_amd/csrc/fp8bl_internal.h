@@ -16,6 +16,15 @@ hipError_t launch_quantize(const float* w, uint8_t* q, float* s,
 hipError_t launch_quantize_bf16(const uint16_t* w, uint8_t* q, float* s,
                                 int64_t n, int64_t k, hipStream_t stream);
 
+// W8A8 route: per-token 1x128 activation quantizer (scales [GK, M]) and the
+// FP8 x FP8 block-scaled GEMM.
+hipError_t launch_act_quantize(const uint16_t* x, uint8_t* xq, float* xs, int64_t m, int64_t k,
+                               hipStream_t stream);
+size_t w8a8_partials_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const float* s,
+                            uint16_t* y, int64_t m, int64_t n, int64_t k, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
 // Large-M fused GEMM (E4M3 tiles decoded to bf16 in registers, bf16 MFMA).
 size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s,

@@ -102,7 +102,60 @@ void quantize_kernel(const T* __restrict__ w, uint8_t* __restrict__ q,
   }
 }
 
+// Activation quantizer of the W8A8 route: per token, per 1x128 K group,
+// the same arithmetic as the weight blocks (S = fl32(amax / 448), 1 for an
+// all-zero group; code = nearest E4M3 of fl32(x / S)). A 256-thread block
+// covers 16 consecutive rows of one K group: 16 lanes per row, 8 bf16 each
+// (one 16-byte load), the group maximum by a 16-lane butterfly. Scales are
+// written K-block-major, xs[kb * M + row], so a block's 16 scales are one
+// contiguous 64-byte run.
+__global__ __launch_bounds__(kThreads)
+void act_quantize_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
+                         float* __restrict__ xs, int M, int K) {
+  const int kb = blockIdx.y;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int col = kb * kBlock + sub * 8;
+  // K % 16 == 0 and col % 8 == 0, so a chunk is wholly inside or outside K
+  const bool ok = row < M && col < K;
+  float v[8];
+  float amax = 0.0f;
+  if (ok) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + (size_t)row * K + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __builtin_bit_cast(float, raw[i] << 16);
+      v[2 * i + 1] = __builtin_bit_cast(float, raw[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+  if (ok) {
+    u32x2 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      out[h] = e4m3_from_f32(__fdiv_rn(v[4 * h], sc)) |
+               (e4m3_from_f32(__fdiv_rn(v[4 * h + 1], sc)) << 8) |
+               (e4m3_from_f32(__fdiv_rn(v[4 * h + 2], sc)) << 16) |
+               (e4m3_from_f32(__fdiv_rn(v[4 * h + 3], sc)) << 24);
+    *reinterpret_cast<u32x2*>(xq + (size_t)row * K + col) = out;
+  }
+  if (sub == 0 && row < M) xs[(size_t)kb * M + row] = sc;
+}
+
 }  // namespace
+
+hipError_t launch_act_quantize(const uint16_t* x, uint8_t* xq, float* xs, int64_t m, int64_t k,
+                               hipStream_t stream) {
+  const int gk = (int)((k + kBlock - 1) / kBlock);
+  const uint64_t rows = ((uint64_t)m + 15) / 16;
+  hipLaunchKernelGGL(act_quantize_kernel, dim3((uint32_t)rows, (uint32_t)gk), dim3(kThreads), 0,
+                     stream, x, xq, xs, (int)m, (int)k);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const float* w, uint8_t* q, float* s, int64_t n, int64_t k,
                            hipStream_t stream) {

@@ -129,6 +129,54 @@ int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate, const float*
                           const uint8_t* q_up, const float* scale_inv_up, uint16_t* h,
                           int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+/* ---- W8A8 route -------------------------------------------------------
+ * FastVideo PR #1829, "Changes", first bullet: the Blackwell route pairs a
+ * groupwise FP8 GEMM with a (Triton) quantizer. Read here as: activations
+ * quantized per token in 1x128 K groups with the weight's arithmetic, and a
+ * GEMM multiplying E4M3 codes exactly, applying x_scale * weight_scale_inv
+ * to each 128-wide K block's fp32 sum. Activation scales are K-block-major:
+ * x_scale[kb * m + row], kb < ceil(k/128). */
+
+/* Per-token activation quantization: for every row and 1x128 group along K
+ * (the last group may be shorter),
+ *   S = fl32(amax / 448)  (1.0 for an all-zero group),
+ *   XQ = nearest finite E4M3 to fl32(x / S), ties to even, saturating.
+ *   x        [m,k] bf16 bits, finite (in, 16-B aligned)
+ *   xq       [m,k] E4M3 bytes (out, 16-B aligned)
+ *   x_scale  [ceil(k/128), m] fp32 (out, 4-B aligned)
+ * Bit-exact. k % 16 == 0. Non-finite x gives unspecified codes. */
+int fp8_act_quantize(const uint16_t* x, uint8_t* xq, float* x_scale, int64_t m, int64_t k,
+                     hipStream_t stream);
+
+/* Bytes of workspace fp8_block_linear_w8a8_bf16 needs (the quantized
+ * activation, its scales and split-K partials); it also suffices for
+ * fp8_block_linear_w8a8. Host only; 0 for empty or invalid shapes. */
+size_t fp8_block_linear_w8a8_workspace_size(int64_t m, int64_t n, int64_t k);
+
+/* W8A8 GEMM on pre-quantized activations:
+ *   y[m,n] = bf16_rne( sum_kb x_scale[kb,m] * S[n/128,kb] *
+ *                      sum_{k in block kb} e4m3(xq[m,k]) * e4m3(q[n,k]) )
+ * with fp32 block sums and fp32 accumulation across blocks.
+ *   xq, x_scale  as written by fp8_act_quantize (in; 16-B / 4-B aligned)
+ *   q, scale_inv the block-FP8 weight, as for fp8_block_linear (in)
+ *   y            [m,n] bf16 bits (out, 16-B aligned, may not overlap)
+ *   workspace    as for fp8_block_linear (fp32 split-K partials), at least
+ *                fp8_block_linear_w8a8_workspace_size bytes or NULL when the
+ *                shape needs none; calls sharing it must be ordered.
+ * K may be at most 2^20. */
+int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t* q,
+                          const float* scale_inv, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The whole W8A8 route from a bf16 activation: fp8_act_quantize into the
+ * workspace, then fp8_block_linear_w8a8. Same result as those two calls.
+ *   x          [m,k] bf16 bits, finite (in, 16-B aligned)
+ *   workspace  at least fp8_block_linear_w8a8_workspace_size bytes,
+ *              256-B aligned (required for every non-empty shape). */
+int fp8_block_linear_w8a8_bf16(const uint16_t* x, const uint8_t* q, const float* scale_inv,
+                               uint16_t* y, int64_t m, int64_t n, int64_t k, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 /* The converter's quantization (FastVideo PR #1829, "Changes", converter
  * bullet: E4M3 weight plus per-128x128 weight_scale_inv). For each block:
  *   amax = max |w| over the elements present in the block,

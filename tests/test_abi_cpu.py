@@ -20,7 +20,8 @@ def test_header_symbols_exported(lib):
         "fp8_block_abi_version", "fp8_block_status_string", "fp8_block_device_supported",
         "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
         "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
-        "fp8_block_mlp_gate_up",
+        "fp8_block_mlp_gate_up", "fp8_act_quantize", "fp8_block_linear_w8a8_workspace_size",
+        "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16",
     }
     for name in names:
         assert hasattr(lib, name), name
@@ -92,6 +93,54 @@ def test_linear_argument_errors(lib, args, status):
 ])
 def test_mlp_gate_up_argument_errors(lib, args, status):
     assert L.mlp_gate_up_raw(*args) == status
+
+
+@pytest.mark.parametrize("m,k,xoff,qoff,soff,status", [
+    (4, 15, 0, 0, 0, L.FP8BL_INVALID_ARG),
+    (-1, 16, 0, 0, 0, L.FP8BL_INVALID_ARG),
+    (4, 0, 0, 0, 0, L.FP8BL_INVALID_ARG),
+    (4, 16, 2, 0, 0, L.FP8BL_ALIGNMENT),
+    (4, 16, 0, 8, 0, L.FP8BL_ALIGNMENT),
+    (4, 16, 0, 0, 2, L.FP8BL_ALIGNMENT),
+    (0, 16, 0, 0, 0, L.FP8BL_OK),
+])
+def test_act_quantize_argument_errors(lib, m, k, xoff, qoff, soff, status):
+    assert L.act_quantize_raw(FAKE + xoff, 8 * FAKE + qoff, 16 * FAKE + soff, m, k) == status
+    assert L.act_quantize_raw(FAKE, FAKE, 16 * FAKE, 4, 16) == L.FP8BL_INVALID_ARG   # xq over x
+    assert L.act_quantize_raw(0, 8 * FAKE, 16 * FAKE, 4, 16) == L.FP8BL_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    # (xq, xs, q, s, y, m, n, k, ws, ws_bytes)
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 4, 8, 15, 0, 0), L.FP8BL_INVALID_ARG),
+    ((0, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 4, 8, 16, 0, 0), L.FP8BL_INVALID_ARG),
+    ((FAKE, 0, 3 * FAKE, 4 * FAKE, 8 * FAKE, 4, 8, 16, 0, 0), L.FP8BL_INVALID_ARG),
+    ((FAKE + 4, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 4, 8, 16, 0, 0), L.FP8BL_ALIGNMENT),
+    ((FAKE, 2 * FAKE + 2, 3 * FAKE, 4 * FAKE, 8 * FAKE, 4, 8, 16, 0, 0), L.FP8BL_ALIGNMENT),
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 2 * FAKE, 4, 8, 16, 0, 0), L.FP8BL_INVALID_ARG),   # y over xs
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 1, 8, (1 << 20) + 16, 0, 0), L.FP8BL_INVALID_ARG),
+    ((FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 0, 8, 16, 0, 0), L.FP8BL_OK),
+])
+def test_w8a8_argument_errors(lib, args, status):
+    assert L.linear_w8a8_raw(*args) == status
+
+
+def test_w8a8_workspace_rules(lib):
+    assert L.w8a8_workspace_size(0, 8, 16) == 0
+    assert L.w8a8_workspace_size(4, 8, 15) == 0
+    m, n, k = 512, 5120, 5120
+    need = L.w8a8_workspace_size(m, n, k)
+    act = -(-m * k // 256) * 256 + -(-(k // 128) * m * 4 // 256) * 256
+    assert need >= act and need % 256 == 0
+    assert need <= act + 8 * (m * n + 64) * 4 + 256
+    x, q, s, y = FAKE, 64 * FAKE, 96 * FAKE, 128 * FAKE
+    # the bf16 entry always needs the workspace (it holds the quantized x)
+    assert L.linear_w8a8_bf16_raw(x, q, s, y, 4, 8, 16, 0, 0) == L.FP8BL_WORKSPACE
+    assert L.linear_w8a8_bf16_raw(x, q, s, y, m, n, k, 256 * FAKE, need - 256) == L.FP8BL_WORKSPACE
+    assert L.linear_w8a8_bf16_raw(x, q, s, y, m, n, k, 256 * FAKE + 16, need) == L.FP8BL_ALIGNMENT
+    assert L.linear_w8a8_bf16_raw(x, q, s, y, m, n, k, y, need) == L.FP8BL_INVALID_ARG
+    # the pre-quantized entry needs it only for split-K shapes
+    assert L.linear_w8a8_raw(x, 32 * FAKE, q, s, y, m, n, k, 0, 0) == L.FP8BL_WORKSPACE
 
 
 def test_linear_workspace_errors(lib):

@@ -1,0 +1,201 @@
+"""GPU parity of the W8A8 route through the C ABI: the per-token activation
+quantizer bit for bit against the oracle, and the E4M3 x E4M3 block-scaled
+GEMM against the oracle's exact fp64 target with the bound
+|y - Y*| <= 2^-7 |Y*| + 1e-4 sum_k |x_k w_k|. The GEMM's inputs (activation
+codes and scales, weight codes and scales) come from the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from workloads import generate, random_problem  # noqa: E402
+
+from gpu_util import bits, f32, say, to_bf16, to_f32, to_u8, u8  # noqa: E402
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+import block_scaled_fp8_linear_amd as F  # noqa: E402
+
+
+def gpu_act_quantize(x_bits):
+    xq, xs = F.fp8_act_quantize(to_bf16(x_bits))
+    torch.cuda.synchronize()
+    return u8(xq), f32(xs)
+
+
+def run_w8a8(xq, xs, q, s):
+    y = F.fp8_block_linear_w8a8(to_u8(xq), to_f32(xs), to_u8(q), to_f32(s))
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def assert_bound(y_bits, y_ref, a_ref, label):
+    ratio = O.gemm_bound_ratio(y_bits, y_ref, a_ref)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    say(label, "max bound ratio", worst)
+    assert worst <= 1.0, (label, worst, np.unravel_index(np.argmax(ratio), ratio.shape))
+
+
+# ---------------------------------------------------------------------------
+# activation quantizer: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,k", [(1, 16), (3, 144), (17, 272), (64, 1024), (130, 784), (513, 5120)])
+def test_act_quantize_shapes(m, k):
+    x, _ = random_problem(m * 31 + k, m, 8, k)
+    say("act quantize", m, k)
+    xq, xs = gpu_act_quantize(x)
+    exq, exs = O.act_quantize(x)
+    assert np.array_equal(xs.view(np.uint32), exs.view(np.uint32)), np.argwhere(xs != exs)[:5]
+    assert np.array_equal(xq, exq), np.argwhere(xq != exq)[:5]
+
+
+def test_act_quantize_special_groups():
+    m, k = 8, 512
+    rng = np.random.default_rng(31)
+    xf = rng.standard_normal((m, k)).astype(np.float32)
+    xf[0] = 0.0                                   # all-zero row: scales 1, codes 0
+    xf[1, :128] = 0.0
+    xf[2] *= 1e-30                                # tiny values (bf16 keeps them)
+    xf[3, 128:256] = -0.0
+    # exact ties: amax = 448 * 2^-3 makes S = 2^-3, so x / S is exact and the
+    # midpoints between E4M3 codes must round to the even code
+    tab = O.e4m3_table()[:0x7F]
+    mids = (tab[1:] + tab[:-1]) / 2.0
+    row = np.resize(np.concatenate([mids, -mids]), 128).astype(np.float64)
+    row[0] = 448.0
+    xf[4, :128] = (row * 2.0 ** -3).astype(np.float32)
+    xf[5, 256:384] = np.float32(2.0 ** -133)      # bf16 subnormal, single group
+    x = O.bf16_rne_bits(xf)
+    assert np.array_equal(O.bf16_bits_to_f32(x[4, :128]).astype(np.float64), row * 2.0 ** -3)
+    say("act quantize special groups")
+    xq, xs = gpu_act_quantize(x)
+    exq, exs = O.act_quantize(x)
+    assert np.array_equal(xs.view(np.uint32), exs.view(np.uint32))
+    assert np.array_equal(xq, exq), np.argwhere(xq != exq)[:5]
+
+
+@pytest.mark.parametrize("name,idx", [("attn_proj", 0), ("dit_large_m", 0)])
+def test_act_quantize_workloads(name, idx):
+    lin = generate(name).linears[idx]
+    say("act quantize workload", name, lin.m, lin.k)
+    xq, xs = gpu_act_quantize(lin.x)
+    exq, exs = O.act_quantize(lin.x)
+    assert np.array_equal(xs.view(np.uint32), exs.view(np.uint32))
+    assert np.array_equal(xq, exq)
+
+
+# ---------------------------------------------------------------------------
+# W8A8 GEMM: bound against the exact target
+# ---------------------------------------------------------------------------
+
+def _w8a8_inputs(seed, m, n, k):
+    x, w = random_problem(seed, m, n, k)
+    xq, xs = O.act_quantize(x)
+    q, s = O.quantize(w)
+    return xq, xs, q, s
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 8, 16), (5, 130, 48), (37, 200, 272), (64, 384, 256), (130, 300, 1040),
+    (256, 256, 512), (300, 520, 784), (129, 129, 4096), (512, 1024, 5120),
+])
+def test_w8a8_small_shapes(m, n, k):
+    xq, xs, q, s = _w8a8_inputs(m * 13 + n * 7 + k, m, n, k)
+    say("w8a8", m, n, k)
+    y = run_w8a8(xq, xs, q, s)
+    yr, ar = O.linear_w8a8_exact(xq, xs, q, s)
+    assert_bound(y, yr, ar, f"w8a8 {m}x{n}x{k}")
+
+
+def test_w8a8_all_codes_pow2_scales():
+    # every finite code on both sides, power-of-two scales that differ per block
+    m, n, k = 256, 256, 512
+    rng = np.random.default_rng(33)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    xq = np.resize(finite, m * k).reshape(m, k).copy()
+    rng.shuffle(xq, axis=1)
+    q = np.resize(finite[::-1], n * k).reshape(n, k).copy()
+    xs = (2.0 ** rng.integers(-10, 4, (4, m))).astype(np.float32)
+    s = (2.0 ** rng.integers(-12, -2, (2, 4))).astype(np.float32)
+    say("w8a8 all codes")
+    y = run_w8a8(xq, xs, q, s)
+    yr, ar = O.linear_w8a8_exact(xq, xs, q, s)
+    assert_bound(y, yr, ar, "w8a8 all codes")
+
+
+def test_w8a8_one_hot_exact():
+    # one non-zero code per row of X: every output is one product, exact
+    m, n, k = 128, 256, 384
+    rng = np.random.default_rng(34)
+    xq = np.zeros((m, k), np.uint8)
+    cols = rng.integers(0, k, m)
+    xq[np.arange(m), cols] = 0x38                  # 1.0
+    xs = np.ones((3, m), np.float32)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    q, s = O.quantize(w)
+    say("w8a8 one-hot")
+    y = run_w8a8(xq, xs, q, s)
+    yr, _ = O.linear_w8a8_exact(xq, xs, q, s)
+    # y = bf16(fl32(e4m3(q) * s)) exactly: one product, one rounding
+    exp = O.bf16_rne_bits(yr.astype(np.float32))
+    assert np.array_equal(y, exp)
+
+
+def test_w8a8_zero_and_empty():
+    xq, xs, q, s = _w8a8_inputs(35, 64, 256, 512)
+    y = run_w8a8(np.zeros_like(xq), xs, q, s)
+    assert np.all((y & 0x7FFF) == 0)
+    y = F.fp8_block_linear_w8a8(to_u8(xq[:0]), to_f32(xs[:, :0]), to_u8(q), to_f32(s))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 256)
+
+
+def test_w8a8_bf16_entry_equals_two_calls_and_reproducible():
+    m, n, k = 512, 5120, 5120                      # split-K shape
+    x, w = random_problem(36, m, n, k)
+    q, s = O.quantize(w)
+    xt, qt, st = to_bf16(x), to_u8(q), to_f32(s)
+    say("w8a8 bf16 entry", m, n, k)
+    ws = torch.empty(F.w8a8_workspace_size(m, n, k), dtype=torch.uint8, device="cuda:0")
+    ws.fill_(0xFF)                                 # garbage must not matter
+    y1 = F.fp8_block_linear_w8a8_bf16(xt, qt, st, workspace=ws)
+    xq, xs = F.fp8_act_quantize(xt)
+    y2 = F.fp8_block_linear_w8a8(xq, xs, qt, st, workspace=ws)
+    y3 = F.fp8_block_linear_w8a8_bf16(xt, qt, st, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    # and the activation codes are the oracle's
+    exq, exs = O.act_quantize(x)
+    assert np.array_equal(u8(xq), exq) and np.array_equal(f32(xs), exs)
+
+
+def _sample_idx(size, rng, n_rand):
+    edges = {0, size - 1, min(127, size - 1), min(128, size - 1)}
+    return np.array(sorted(edges | set(rng.integers(0, size, n_rand).tolist())), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name,idx", [("attn_proj", 0), ("mlp_pair", 0), ("dit_large_m", 0),
+                                      ("dit_large_m", 1)])
+def test_w8a8_workloads_sampled(name, idx):
+    lin = generate(name).linears[idx]
+    xq, xs = O.act_quantize(lin.x)
+    q, s = O.quantize(lin.w)
+    say("w8a8 workload", name, lin.name, lin.m, lin.n, lin.k)
+    y = run_w8a8(xq, xs, q, s)
+    rng = np.random.default_rng(lin.m + lin.n)
+    ms = _sample_idx(lin.m, rng, 24)
+    ns = _sample_idx(lin.n, rng, 24)
+    mm, nn = np.meshgrid(ms, ns, indexing="ij")
+    mm, nn = mm.ravel(), nn.ravel()
+    yr, ar = O.linear_w8a8_sampled(xq, xs, q, s, mm, nn)
+    assert_bound(y[mm, nn], yr, ar, f"w8a8 {name}/{lin.name} ({mm.size} sampled)")
+    assert np.all((y & 0x7F80) != 0x7F80)
