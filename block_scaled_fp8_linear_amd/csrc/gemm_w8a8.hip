@@ -29,6 +29,13 @@
 //
 // Split-K over K blocks (gridDim.y > 1) writes fp32 partial tiles that the
 // ordered reduce kernel sums, as in the bf16 path.
+//
+// Measured on MI355X (16384x3072x3072): the step is bound by L2 -> CU
+// delivery (~10 TB/s aggregate, 85% L2 hits), not by the matrix cores; the
+// same kernel without its MFMAs runs within 15% of the full one. Tried and
+// not faster: 256x128 tiles with 8 waves and a three-stage direct-to-LDS
+// ring (one workgroup per CU), with and without software-pipelined operand
+// reads. Fewer bytes per flop (larger tiles) is what would move it.
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
@@ -96,13 +103,14 @@ void gemm_w8a8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ 
   const int sr = tid >> 3;
   const uint32_t off0 = (uint32_t)(sr * K + ch * 16);
   const uint32_t row32 = (uint32_t)(32 * K);
-  // activation scales: threads 0..31 move 4 consecutive rows each
-  const int srow = m0 + (tid & 31) * 4;
+  // activation scales: thread moves row (tid & 127) of the tile; the two
+  // halves of the workgroup load and store identical values (no branch)
+  const int srow = m0 + (tid & 127);
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(xs, (uint32_t)((size_t)gk * M * 4));
   const float* __restrict__ wsc = s + (size_t)tn * gk;
 
   u32x4 xr[4], wr[4];
-  f32x4v sv;
+  float sv;
   auto load = [&](int kb) {
     const bool kin = kb < kb1 && kb * kTile + ch * 16 < K;
     const uint32_t base = (uint32_t)(kb * kTile);
@@ -111,13 +119,10 @@ void gemm_w8a8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ 
       xr[i] = buf_load16(xrs, kin ? off0 + i * row32 + base : kOob);
       wr[i] = buf_load16(wrs, kin ? off0 + i * row32 + base : kOob);
     }
-    // rows past M and steps past the split read zero (no branch)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool sin = tid < 32 && kb < kb1 && srow + j < M;
-      sv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                  srs, sin ? (uint32_t)((kb * M + srow + j) * 4) : kOob, 0, 0));
-    }
+    // rows past M and steps past the split read zero
+    const bool sin = kb < kb1 && srow < M;
+    sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+             srs, sin ? (uint32_t)((kb * M + srow) * 4) : kOob, 0, 0));
   };
   auto store = [&](int buf) {
 #pragma unroll
@@ -125,7 +130,7 @@ void gemm_w8a8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ 
       *reinterpret_cast<u32x4*>(&at[buf][tile_off(sr + 32 * i, ch)]) = xr[i];
       *reinterpret_cast<u32x4*>(&bt[buf][tile_off(sr + 32 * i, ch)]) = wr[i];
     }
-    if (tid < 32) *reinterpret_cast<f32x4v*>(&sx[buf][tid * 4]) = sv;
+    sx[buf][tid & 127] = sv;
   };
 
   f32x4v acc[4][4];
@@ -182,6 +187,9 @@ void gemm_w8a8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ 
         for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], scl[i][r], acc[i][j][r]);
       }
     __builtin_amdgcn_s_setprio(0);
+    // Keep the staging writes behind the MFMAs: they wait for this step's
+    // global loads, which then have the whole MFMA phase to arrive.
+    __builtin_amdgcn_sched_barrier(0);
     store(cur ^ 1);
     __syncthreads();
   }
