@@ -64,7 +64,11 @@ __device__ __forceinline__ int xs_offset(int row, int chunk) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // dword 3 = 0x00020000: raw (untyped) buffer, 32-bit data format, the
   // layout gfx9-family descriptors use; out-of-range reads return zero.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  // The size is wave-uniform, but without the readfirstlane the compiler
+  // computed it in VALU for the weight descriptor and wrapped every weight
+  // load in a waterfall loop.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -355,54 +359,53 @@ void gemm_gated_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 }
 
 struct TiledPlan {
-  int cfg;          // 0: 128x256, 1: 256x128, 2: 128x128 (all 2 workgroups per CU)
+  int cfg;          // 0: 128x256, 1: 256x128, 2: 128x128
   int bm, bn, splits, kt_per_split;
 };
 
-// Tile choice, from measurements on MI355X (fp8 weight, bf16 X):
-//  - M >= 2048: 128x256 tiles; four waves share a 128-row X tile and each
-//    decodes 64 weight rows.
-//  - smaller M with enough 256x128 tiles to cover every CU: 256x128, which
-//    halves the number of times each weight element is decoded.
-//  - otherwise 128x128 tiles with K split until there are >= ~512 work items
-//    (partials summed in split order by a second kernel).
+// Tile and split choice from a cost model fitted to measurements on MI355X.
+// Work is counted in 128x128x64 MFMA steps; a CU runs its workgroups two
+// (128x256, 256x128: 240+ VGPRs) or three (128x128) at a time, and its
+// throughput depends on how many it holds (steps per microsecond, below).
+// The busiest CU sets the time: ceil(W / 256) workgroups of W, each taking
+// ceil(nkt / splits) steps. K splits add the fp32 partials' round trip
+// (4 bytes per output and split written and read back, 2 bytes of bf16
+// out, at ~5 TB/s). Large square-ish shapes favour the 128x256 tile (more
+// reuse per load); shapes whose 128x128 tiles fill the CUs more evenly
+// (e.g. 2048x5120x5120, 1024x8192x8192, 3072^3) favour 128x128; 512-row
+// text-encoder shapes with few tiles split K.
+double cu_rate(int cfg, int64_t per_cu) {
+  if (cfg == 2) return per_cu <= 1 ? 0.91 : per_cu == 2 ? 1.56 : 1.70;
+  return per_cu <= 1 ? 1.44 : 1.90;
+}
+
 TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
   const int nkt = (int)((k + kBK - 1) / kBK);
-  TiledPlan p{0, 128, 256, 1, nkt};
-  if (m < 2048) {
-    const int64_t t256 = ((m + 255) / 256) * ((n + 127) / 128);
-    if (t256 >= 256) {
-      p = TiledPlan{1, 256, 128, 1, nkt};
-    } else {
-      p = TiledPlan{2, 128, 128, 1, nkt};
-    }
-  }
-  const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + p.bn - 1) / p.bn);
-  // Fewer tiles than CUs: split K. The split count minimises a cost model:
-  // the busiest CU runs ceil(W / 256) of the W workgroups (one alone runs
-  // at ~60% of a pair's rate), each for ceil(nkt / s) steps, and the fp32
-  // partials cost 4 bytes per output and split to write and read back, plus
-  // 2 bytes of bf16 output, at ~5 TB/s. Measured on the M=512 text-encoder
-  // shapes (160 tiles of 128x128): 3 splits (480 workgroups, at most two per
-  // CU) beat 4 (640, up to three per CU). 400 tiles of 256x128 run best
-  // unsplit (the partials' round trip costs more than the idle slots).
-  int splits = 1;
-  if (tiles < 256) {
-    const double kStepUs = 0.75;              // one 128x128 step, two workgroups per CU
-    double best = 1e30;
+  // evaluation order breaks ties: 256x128 first below 2048 rows
+  const int order_small[3] = {1, 0, 2}, order_large[3] = {0, 1, 2};
+  const int* order = m < 2048 ? order_small : order_large;
+  TiledPlan best{2, 128, 128, 1, nkt};
+  double best_cost = 1e30;
+  for (int oi = 0; oi < 3; ++oi) {
+    const int cfg = order[oi];
+    const int bm = cfg == 1 ? 256 : 128, bn = cfg == 0 ? 256 : 128;
+    const int units = cfg == 2 ? 1 : 2;
+    const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
     for (int sp = 1; sp <= 8; ++sp) {
       const int steps = (nkt + sp - 1) / sp;
       if (sp > 1 && steps < 8) break;
-      const int64_t w = tiles * sp;
-      const double load = w <= 256 ? 1.67 : (double)((w + 255) / 256);
-      double cost = load * steps * kStepUs;
+      const int64_t per_cu = (tiles * sp + 255) / 256;
+      double cost = (double)per_cu * steps * units / cu_rate(cfg, per_cu);
       if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
-      if (cost < best) { best = cost; splits = sp; }
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = TiledPlan{cfg, bm, bn, sp, steps};
+      }
     }
   }
-  p.kt_per_split = (nkt + splits - 1) / splits;
-  p.splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
-  return p;
+  best.kt_per_split = best.splits > 1 ? (nkt + best.splits - 1) / best.splits : nkt;
+  best.splits = (nkt + best.kt_per_split - 1) / best.kt_per_split;
+  return best;
 }
 
 }  // namespace
