@@ -15,6 +15,10 @@ hand-written HIP) provides:
 * ``fp8_block_linear_w8a8(xq, x_scale, q, s)`` / ``fp8_block_linear_w8a8_bf16(x, q, s)``
   -> bf16 Y from E4M3 x E4M3 products on the FP8 matrix cores (W8A8 route)
 
+``block_scaled_fp8_linear_amd.checkpoint`` converts a state dict into the
+serialized block-FP8 checkpoint (quantization on the GPU, safetensors shards,
+index and ``quantization_config``).
+
 The functions here only marshal torch tensors (device memory and the current
 stream) into the C ABI declared in include/fp8bl.h; all arithmetic runs in
 the HIP kernels. There is no CPU fallback: without the built library every
