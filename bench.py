@@ -46,6 +46,21 @@ WORKLOADS = {
 }
 
 
+# What one timed launch (one library call per step) runs on the GPU; the
+# rocprofv3 summaries list these kernels with their own averages, which add
+# up to avg_launch_us.
+LAUNCH_KERNELS = {
+    "linear": "fp8_block_linear: gemm_tiled_kernel or gemm_skinny_kernel, "
+              "+ reduce_partials_kernel when K is split",
+    "dequant": "fp8_block_dequant: dequant_kernel",
+    "quantize": "fp8_block_quantize: quantize_kernel<float>",
+    "mlp": "fp8_block_mlp_gate_up: gemm_gated_kernel",
+    "w8a8": "fp8_block_linear_w8a8_bf16: act_quantize_kernel + gemm_w8a8_kernel, "
+            "+ reduce_partials_kernel when K is split",
+    "w8a8_gemm": "fp8_block_linear_w8a8: gemm_w8a8_kernel, + reduce_partials_kernel when K is split",
+}
+
+
 def kernel_source_sha():
     """Hash of the HIP sources: traffic figures taken from counters belong to
     the kernels they were measured on and are dropped once these change."""
@@ -303,6 +318,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(args.workload if args.op == "linear" else f"{args.op}:{args.workload}"),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "launch": LAUNCH_KERNELS[args.op],
             "alg_bytes": abytes,
             "flops": flops,
         },
