@@ -16,7 +16,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;     // every dimension fits int32
-constexpr int64_t kMaxElems = (int64_t)1 << 35;   // N*K, M*K and M*N (8-element chunk index fits uint32)
+constexpr int64_t kMaxElems = (int64_t)1 << 35;   // N*K, M*K and M*N stay below this (8-element chunk index fits uint32)
 constexpr int kSkinnyMaxM = 32;
 // The GEMM kernels address a tile's rows with 32-bit buffer offsets.
 constexpr int64_t kMaxLinearK = (int64_t)1 << 20;
@@ -37,7 +37,7 @@ size_t grid_elems(int64_t n, int64_t k) {
 
 int check_nk(int64_t n, int64_t k) {
   if (n < 0 || k <= 0 || (k % 16) != 0) return FP8BL_INVALID_ARG;
-  if (n >= kMaxDim || k >= kMaxDim || (n > 0 && n * k > kMaxElems)) return FP8BL_INVALID_ARG;
+  if (n >= kMaxDim || k >= kMaxDim || (n > 0 && n * k >= kMaxElems)) return FP8BL_INVALID_ARG;
   if ((n + FP8BL_BLOCK - 1) / FP8BL_BLOCK > 65535) return FP8BL_INVALID_ARG;
   return FP8BL_OK;
 }
@@ -67,8 +67,8 @@ int validate_linear(const uint16_t* x, const uint8_t* q, const float* s, const u
   int st = check_nk(n, k);
   if (st != FP8BL_OK) return st;
   if (k > kMaxLinearK) return FP8BL_INVALID_ARG;
-  if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
-  if (m > 0 && n > 0 && m * n > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && m * k >= kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && n > 0 && m * n >= kMaxElems) return FP8BL_INVALID_ARG;
   if (m == 0 || n == 0) return FP8BL_OK;
   if (!x || !q || !s || !y) return FP8BL_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(s, 4))
@@ -92,8 +92,8 @@ int validate_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const fl
   int st = check_nk(n, k);
   if (st != FP8BL_OK) return st;
   if (k > kMaxLinearK) return FP8BL_INVALID_ARG;
-  if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
-  if (m > 0 && n > 0 && m * n > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && m * k >= kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && n > 0 && m * n >= kMaxElems) return FP8BL_INVALID_ARG;
   if (m == 0 || n == 0) return FP8BL_OK;
   if (!xq || !xs || !q || !s || !y) return FP8BL_INVALID_ARG;
   if (!aligned(xq, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(s, 4))
@@ -212,7 +212,7 @@ FP8BL_EXPORT int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate,
 FP8BL_EXPORT int fp8_act_quantize(const uint16_t* x, uint8_t* xq, float* x_scale, int64_t m,
                                   int64_t k, hipStream_t stream) {
   if (m < 0 || k <= 0 || (k % 16) != 0 || m >= kMaxDim || k >= kMaxDim) return FP8BL_INVALID_ARG;
-  if (m > 0 && m * k > kMaxElems) return FP8BL_INVALID_ARG;
+  if (m > 0 && m * k >= kMaxElems) return FP8BL_INVALID_ARG;
   if ((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK > 65535) return FP8BL_INVALID_ARG;
   if (m == 0) return FP8BL_OK;
   if (!x || !xq || !x_scale) return FP8BL_INVALID_ARG;

@@ -19,7 +19,7 @@
  *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
  *   - Row-major, contiguous. Dimensions are int64_t; zero rows or columns is a
  *     no-op that returns FP8BL_OK. K must be a positive multiple of 16; each
- *     dimension is below 2^31 and each matrix has at most 2^35 elements.
+ *     dimension is below 2^31 and each matrix has fewer than 2^35 elements.
  *   - Data pointers must be 16-byte aligned (scale grids 4-byte aligned,
  *     workspaces 256-byte aligned). Outputs must not overlap inputs.
  *   - Every argument error is reported by the return code BEFORE anything is

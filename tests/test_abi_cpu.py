@@ -68,6 +68,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced here
     ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 8, 16, 0, 0, 7), L.FP8BL_INVALID_ARG),    # bad path
     ((FAKE, FAKE, FAKE, 4 * FAKE, 1 << 31, 8, 16, 0, 0, 0), L.FP8BL_INVALID_ARG),  # M too big
     ((FAKE, FAKE, FAKE, 4 * FAKE, 1, 8, (1 << 20) + 16, 0, 0, 0), L.FP8BL_INVALID_ARG),  # K too big
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 1 << 19, 1 << 16, 1 << 16, 0, 0, 0), L.FP8BL_INVALID_ARG),  # M*K = 2^35
     ((FAKE, FAKE, FAKE, 4 * FAKE, 0, 8, 16, 0, 0, 0), L.FP8BL_OK),             # empty M: no-op
     ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 0, 16, 0, 0, 0), L.FP8BL_OK),             # empty N: no-op
     ((0, 0, 0, 0, 0, 0, 16, 0, 0, 0), L.FP8BL_OK),                             # empty, null ok
@@ -184,3 +185,11 @@ def test_dequant_and_quantize_argument_errors(lib, n, k, qoff, soff, woff, statu
     assert L.quantize_bf16_raw(w, q, s, n, k) == status
     # overlapping output
     assert L.dequant_raw(FAKE, 8 * FAKE, FAKE, 8, 16) == L.FP8BL_INVALID_ARG
+
+
+def test_element_count_limit_is_strict(lib):
+    # 2^35 elements would wrap the kernels' 32-bit 8-element chunk index
+    n, k = 1 << 19, 1 << 16
+    assert L.dequant_raw(FAKE, 8 * FAKE, 16 * FAKE, n, k) == L.FP8BL_INVALID_ARG
+    assert L.quantize_raw(FAKE, 8 * FAKE, 16 * FAKE, n, k) == L.FP8BL_INVALID_ARG
+    assert L.act_quantize_raw(FAKE, 8 * FAKE, 16 * FAKE, n, k) == L.FP8BL_INVALID_ARG

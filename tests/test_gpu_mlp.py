@@ -129,3 +129,22 @@ def test_mlp_pair_workload_sampled():
     assert r.max() <= 1.0
     # the full output has no NaN/inf
     assert np.all((h & 0x7F80) != 0x7F80)
+
+
+def test_mlp_graph_replay_matches_eager():
+    m, n, k = 256, 640, 1024
+    x, qg, sg, qu, su = _pair(8, m, n, k)
+    args = (to_bf16(x), to_u8(qg), to_f32(sg), to_u8(qu), to_f32(su))
+    say("mlp graph replay", m, n, k)
+    eager = bits(F.fp8_block_mlp_gate_up(*args))
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        F.fp8_block_mlp_gate_up(*args, out=out)
+    for rep in range(3):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), rep
+        F.fp8_block_mlp_gate_up(*args)
+        torch.cuda.synchronize()

@@ -288,6 +288,23 @@ def test_linear_graph_replay_matches_eager(m, n, k):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_linear_largest_k_sampled(path):
+    """K at the interface's limit (2^20): 16384 tiled K steps or 4096 skinny
+    super-steps, 8192 scale blocks per row; outputs sampled against Y*."""
+    m, n, k = 32, 256, 1 << 20
+    rng = np.random.default_rng(38)
+    x = O.bf16_rne_bits(rng.standard_normal((m, k), dtype=np.float32)) & np.uint16(0xFFFF)
+    w = (rng.standard_normal((n, k), dtype=np.float32) * 0.02).astype(np.float32)
+    q, s = O.quantize(w)
+    say("largest K", path, m, n, k)
+    y = run_linear(x, q, s, PATHS[path])
+    ms = np.array([0, 7, 31, 16]); ns = np.array([0, 255, 128, 3])
+    mm, nn = np.meshgrid(ms, ns, indexing="ij")
+    yr, ar = O.linear_sampled(x, q, s, mm.ravel(), nn.ravel())
+    assert_bound(y[mm.ravel(), nn.ravel()], yr, ar, f"largest K {path}")
+
+
 def test_linear_empty_shapes():
     say("empty shapes")
     q = to_u8(np.zeros((8, 32), np.uint8))

@@ -199,3 +199,43 @@ def test_w8a8_workloads_sampled(name, idx):
     yr, ar = O.linear_w8a8_sampled(xq, xs, q, s, mm, nn)
     assert_bound(y[mm, nn], yr, ar, f"w8a8 {name}/{lin.name} ({mm.size} sampled)")
     assert np.all((y & 0x7F80) != 0x7F80)
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 5120, 5120), (300, 1024, 1040)])
+def test_w8a8_graph_replay_matches_eager(m, n, k):
+    """The bf16-input W8A8 call (quantizer + GEMM + reduce when split)
+    captured in a HIP graph and replayed with eager work in between gives the
+    eager bits every time."""
+    x, w = random_problem(m + n + k, m, n, k)
+    q, s = O.quantize(w)
+    xt, qt, st = to_bf16(x), to_u8(q), to_f32(s)
+    ws = torch.empty(F.w8a8_workspace_size(m, n, k), dtype=torch.uint8, device="cuda:0")
+    say("w8a8 graph replay", m, n, k)
+    eager = bits(F.fp8_block_linear_w8a8_bf16(xt, qt, st, workspace=ws))
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        F.fp8_block_linear_w8a8_bf16(xt, qt, st, out=out, workspace=ws)
+    for rep in range(3):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), rep
+        F.fp8_block_linear_w8a8_bf16(xt, qt, st, workspace=ws)
+        torch.cuda.synchronize()
+
+
+def test_w8a8_largest_k_sampled():
+    """K at the interface's limit (2^20): 8192 scale blocks per row."""
+    m, n, k = 32, 256, 1 << 20
+    rng = np.random.default_rng(37)
+    x = O.bf16_rne_bits(rng.standard_normal((m, k), dtype=np.float32))
+    w = (rng.standard_normal((n, k), dtype=np.float32) * 0.02).astype(np.float32)
+    xq, xs = O.act_quantize(x)
+    q, s = O.quantize(w)
+    say("w8a8 largest K", m, n, k)
+    y = run_w8a8(xq, xs, q, s)
+    ms = np.array([0, 5, 31, 17]); ns = np.array([0, 255, 128, 77])
+    mm, nn = np.meshgrid(ms, ns, indexing="ij")
+    yr, ar = O.linear_w8a8_sampled(xq, xs, q, s, mm.ravel(), nn.ravel())
+    assert_bound(y[mm.ravel(), nn.ravel()], yr, ar, "w8a8 largest K")
