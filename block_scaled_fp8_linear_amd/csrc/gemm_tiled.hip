@@ -19,8 +19,9 @@
 // Pipeline (one barrier per K step): a wave dequantizes the codes of step k
 // (loaded one step earlier), issues the loads of X and codes for step k+1,
 // runs step k's MFMAs from LDS and the decoded registers, then stages X for
-// step k+1 into the other LDS buffer. Two workgroups share each CU, so one
-// workgroup's decode overlaps the other's MFMAs. Loads go through buffer
+// step k+1 into the other LDS buffer. Two or three workgroups share each CU
+// (three with 128x128 tiles), so one workgroup's decode overlaps another's
+// MFMAs. Loads go through buffer
 // descriptors covering only the tile's valid rows: rows past M or N and the
 // K tail read as zero without branches. (Measured alternatives that did not
 // pay on MI355X: decoding step k+1 inside step k's MFMA stream with two
@@ -278,8 +279,12 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
         for (int t = 0; t < 4; ++t) decode_t(wb2, wr2, sc2, t);
       }
       // Branch-free step (one basic block for the scheduler): past the last
-      // step these loads read zero and the staged tile goes unused.
+      // step these loads read zero and the staged tile goes unused. X is
+      // issued first: its staging at the end of this step then waits only
+      // for the X loads, and the code loads stay in flight across the
+      // barrier until the next step's decode needs them.
       load_x(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
       load_w(wr, kt + 1);
       if constexpr (GATED) load_w2(wr2, kt + 1);
       // Raise this wave's issue priority while it feeds the matrix core, so
