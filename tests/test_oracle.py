@@ -108,6 +108,22 @@ def test_bf16_two_implementations_agree_exhaustive():
         assert np.array_equal(O.bf16_rne_bits(x), O.bf16_rne_bits_nearest(x)), hex(start)
 
 
+@pytest.mark.skipif(os.environ.get("FP8BL_EXHAUSTIVE") != "1",
+                    reason="all fp32 patterns with |v| <= 480; set FP8BL_EXHAUSTIVE=1 (minutes)")
+def test_e4m3_two_encoders_agree_exhaustive():
+    """Table search and bit manipulation give the same code for every fp32
+    bit pattern of magnitude <= 480 (both signs): past 448 both saturate."""
+    top = int(np.array([480.0], np.float32).view(np.uint32)[0])
+    step = 1 << 24
+    for sign in (0, 0x80000000):
+        for start in range(0, top + 1, step):
+            stop = min(start + step, top + 1)
+            pats = (np.arange(start, stop, dtype=np.uint64) | sign).astype(np.uint32)
+            v = pats.view(np.float32)
+            a, b = O.e4m3_encode_nearest(v), O.e4m3_encode_bits(v)
+            assert np.array_equal(a, b), (hex(sign), hex(start), np.argwhere(a != b)[:3])
+
+
 def test_bf16_spot_values():
     cases = {
         0x3F800000: 0x3F80,   # 1.0
