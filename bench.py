@@ -109,14 +109,21 @@ def cpu_baseline(lin, x_bits, budget_s=12.0):
     q, s = O.quantize(lin.w)
     m_all = x_bits.shape[0]
 
+    split = {"dequant_s": 0.0, "matmul_s": 0.0}
+
     def one_pass(rows):
         t0 = time.perf_counter()
         wd = O.dequant(q, s)
+        t1 = time.perf_counter()
         O.linear_exact(x_bits[:rows], wd)
-        return time.perf_counter() - t0
+        t2 = time.perf_counter()
+        split["dequant_s"] += t1 - t0
+        split["matmul_s"] += t2 - t1
+        return t2 - t0
 
     rows = 1
     while True:
+        split["dequant_s"] = split["matmul_s"] = 0.0
         dt = one_pass(rows)
         if dt * 2.5 > budget_s or rows >= m_all:
             break
@@ -134,10 +141,46 @@ def cpu_baseline(lin, x_bits, budget_s=12.0):
         "kind": "oracle",
         "sample": f"{what} of X against the full {lin.n}x{lin.k} weight (dequant + fp64 Y* and "
                   f"sum|x w|), {total_t:.2f} s",
+        "cpu_model": cpu_model(),
+        "dequant_s": round(split["dequant_s"], 3),
+        "matmul_s": round(split["matmul_s"], 3),
         "seconds": total_t,
         "rows": rows,
         "passes": passes,
     }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stream_ceiling(nbytes=1 << 30, reps=10):
+    """A plain library streaming read (torch's sum over a large bf16 tensor)
+    and copy on the device: the practical HBM ceilings the HBM-bound kernels
+    are compared with."""
+    import torch
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        x.sum(); y.copy_(x)
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn, moved in (("read", lambda: x.sum(), nbytes), ("copy", lambda: y.copy_(x), 2 * nbytes)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_GBps"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    return out
 
 
 def main():
@@ -159,6 +202,8 @@ def main():
                     help="time K separate calls instead of one replay of a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only time a plain 1 GiB streaming read and copy (practical HBM ceilings) and exit")
     args = ap.parse_args()
 
     if args.copy_calibration:
@@ -169,6 +214,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "launches": 5}))
+        return
+
+    if args.stream_ceiling:
+        print(json.dumps({"stream_ceiling": stream_ceiling()}))
         return
 
     if args.gpus != 1:
@@ -336,6 +385,10 @@ def main():
             "flops": flops,
         },
     }
+    if args.op == "linear" and bound == "hbm":
+        # the weight stream alone (codes + scale grid), the part that scales with N*K
+        wbytes = n * k + 4 * gn * gk
+        out["roofline"]["weight_GBps"] = round(wbytes / avg_launch_s / 1e9, 1)
     if not args.no_cpu_baseline and args.op == "linear":
         cb = cpu_baseline(lin, x_bits)
         rows, passes = cb.pop("rows"), cb.pop("passes")
