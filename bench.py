@@ -171,7 +171,7 @@ def stream_ceiling(nbytes=1 << 30, reps=10):
         x.sum(); y.copy_(x)
     torch.cuda.synchronize()
     out = {}
-    for name, fn, moved in (("read", lambda: x.sum(), nbytes), ("copy", lambda: y.copy_(x), 2 * nbytes)):
+    for name, fn, moved in (("torch_sum_read", lambda: x.sum(), nbytes), ("torch_copy", lambda: y.copy_(x), 2 * nbytes)):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
