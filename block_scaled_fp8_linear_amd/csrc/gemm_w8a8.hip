@@ -30,12 +30,16 @@
 // Split-K over K blocks (gridDim.y > 1) writes fp32 partial tiles that the
 // ordered reduce kernel sums, as in the bf16 path.
 //
-// Measured on MI355X (16384x3072x3072): the step is bound by L2 -> CU
-// delivery (~10 TB/s aggregate, 85% L2 hits), not by the matrix cores; the
-// same kernel without its MFMAs runs within 15% of the full one. Tried and
-// not faster: 256x128 tiles with 8 waves and a three-stage direct-to-LDS
-// ring (one workgroup per CU), with and without software-pipelined operand
-// reads. Fewer bytes per flop (larger tiles) is what would move it.
+// Measured on MI355X (16384x3072x3072): the step is bound by LDS bandwidth.
+// Per workgroup step the four waves read 16 KB each of A and B fragments
+// and the tile is staged with 32 KB of writes; the same kernel without its
+// global loads runs within 20% of the full one, without its MFMAs within
+// 18%, while the global -> LDS staging alone takes 14% of the time. Tried
+// and slower: B fragments loaded from memory straight into registers (1.6x
+// slower: 16-row x 64-byte loads), 256x128 tiles with 8 waves and a
+// three-stage direct-to-LDS ring (no faster). Larger per-wave tiles (fewer
+// LDS bytes per MFMA) are what would move it, at a register cost that
+// leaves one workgroup per CU.
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
