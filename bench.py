@@ -61,30 +61,65 @@ LAUNCH_KERNELS = {
 }
 
 
-def kernel_source_sha():
-    """Hash of the HIP sources: traffic figures taken from counters belong to
-    the kernels they were measured on and are dropped once these change."""
+# Source files behind each kernel (besides the shared device/launch files):
+# a traffic figure stays valid while the files of the kernels it was measured
+# on are unchanged.
+KERNEL_SOURCES = {
+    "gemm_tiled_kernel": ("gemm_tiled.hip",),
+    "gemm_gated_kernel": ("gemm_tiled.hip",),
+    "gemm_skinny_kernel": ("gemm_skinny.hip",),
+    "reduce_partials_kernel": ("gemm_skinny.hip",),
+    "dequant_kernel": ("dequant.hip",),
+    "quantize_kernel": ("quantize.hip",),
+    "act_quantize_kernel": ("quantize.hip",),
+    "gemm_w8a8_kernel": ("gemm_w8a8.hip",),
+}
+SHARED_SOURCES = ("fp8bl_api.hip", "fp8bl_device.h", "fp8bl_internal.h")
+
+
+def kernel_source_sha(kernels=None, read=None):
+    """Hash of the HIP sources of ``kernels`` (names as rocprofv3 prints them,
+    template arguments allowed) plus the shared device and launch files; all
+    of csrc when ``kernels`` is None. ``read(name) -> bytes`` supplies file
+    contents (default: the working tree)."""
     import glob
     import hashlib
-    h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp8_linear_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    if read is None:
+        read = lambda name: open(os.path.join(csrc, name), "rb").read()
+    if kernels is None:
+        names = sorted(os.path.basename(f) for f in glob.glob(os.path.join(csrc, "*")))
+    else:
+        names = set(SHARED_SOURCES)
+        for kname in kernels:
+            base = kname.split("<")[0].strip()
+            if base not in KERNEL_SOURCES:
+                raise KeyError(f"no source files recorded for kernel {kname!r}")
+            names.update(KERNEL_SOURCES[base])
+        names = sorted(names)
+    h = hashlib.sha256()
+    for name in names:
+        h.update(name.encode())
+        h.update(read(name))
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None
-    if there is none for this workload or the kernels changed since."""
+    if there is none for this workload or its kernels' sources changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         data = json.load(open(path))
     except (OSError, ValueError):
         return None
     ent = data.get("workloads", {}).get(workload)
-    if not ent or data.get("kernel_source_sha") != kernel_source_sha():
+    if not ent or not ent.get("kernels") or ent.get("source_sha") is None:
+        return None
+    try:
+        if ent["source_sha"] != kernel_source_sha(ent["kernels"]):
+            return None
+    except (OSError, KeyError):
         return None
     return ent.get("hbm_bytes_per_launch")
 

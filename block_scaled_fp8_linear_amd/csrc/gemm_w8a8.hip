@@ -16,9 +16,9 @@
 // Workgroup tile 128x128, 4 waves in a 2x2 grid, 64x64 per wave (4x4 MFMA
 // blocks). X and W tiles (128 rows x 128 bytes each per step) and the tile's
 // 128 activation scales are staged through LDS, double-buffered with one
-// barrier per step; rows use the same XOR swizzle of 16-byte chunks as the
-// bf16 path, so the MFMA operand reads (16 rows at one chunk) are
-// conflict-free. The weight scale is uniform per workgroup and step (the
+// barrier per step; 16-byte chunks are XOR-swizzled per row (see tile_off)
+// so the MFMA operand reads and the row-wise staging writes are both free of
+// bank conflicts. The weight scale is uniform per workgroup and step (the
 // N tile is one 128-row scale block).
 //
 // MFMA operand layout: lane l supplies 32 bytes (32 codes) of row l % 16 of
@@ -32,12 +32,14 @@
 //
 // Measured on MI355X (16384x3072x3072): the step is bound by LDS bandwidth.
 // Per workgroup step the four waves read 16 KB each of A and B fragments
-// and the tile is staged with 32 KB of writes; the same kernel without its
-// global loads runs within 20% of the full one, without its MFMAs within
-// 18%, while the global -> LDS staging alone takes 14% of the time. Tried
-// and slower: B fragments loaded from memory straight into registers (1.6x
+// and the tile is staged with 32 KB of writes: at full MFMA rate that is as
+// many LDS cycles as MFMA cycles. The same kernel without its global loads
+// runs within 20% of the full one, without its MFMAs within 18%, while the
+// global -> LDS staging alone takes 14% of the time. Tried and slower or no
+// faster: B fragments loaded from memory straight into registers (1.6x
 // slower: 16-row x 64-byte loads), 256x128 tiles with 8 waves and a
-// three-stage direct-to-LDS ring (no faster). Larger per-wave tiles (fewer
+// three-stage direct-to-LDS ring, the weight scale loaded one step ahead
+// with the operand reads in first-use order. Larger per-wave tiles (fewer
 // LDS bytes per MFMA) are what would move it, at a register cost that
 // leaves one workgroup per CU.
 #include "fp8bl_device.h"
@@ -65,8 +67,13 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` (128 bytes).
+// The operand read has lanes 16g..16g+15 on 16 consecutive rows at chunk
+// 2g (+1). Measured with SQ_LDS_BANK_CONFLICT on gfx950: XOR with
+// (row >> 1) & 7 (the bf16 path's swizzle, conflict-free for its 32-row
+// reads) costs 4 extra cycles per ds_read_b128 here; XOR with row & 7 and
+// row bit 3 has none, for these reads and for the 8-lanes-per-row writes.
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * kTile + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * kTile + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
 }
 
 __global__ __launch_bounds__(kThreads, 2)
