@@ -88,6 +88,23 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float acc_g, float acc_u) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Order of a step's MFMA phase: the X fragment reads (one ds_read_b128 per
+// fragment, 4 * MB per step) run kReadsAhead fragments in front of the MFMAs
+// that consume them, each fragment feeding PER_FRAG MFMAs. Left to itself
+// the compiler issued each read pair right before its MFMAs and waited for
+// it there, exposing the LDS latency every few MFMAs (measured 2-6% slower
+// across the workloads).
+template <int MB, int PER_FRAG>
+__device__ __forceinline__ void schedule_operand_reads() {
+  constexpr int kReadsAhead = 4;
+  __builtin_amdgcn_sched_group_barrier(0x100, kReadsAhead, 0);     // DS reads
+#pragma unroll
+  for (int i = 0; i < 4 * MB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, PER_FRAG, 0);      // MFMAs
+    if (i + kReadsAhead < 4 * MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // GATED: the MLP gate/up pair in one pass. The same X tile feeds two weights
 // (q, s = gate; q2, s2 = up) into two accumulator sets and the epilogue
 // writes swiglu(gate, up) instead of either product.
@@ -236,6 +253,7 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
         for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb[nb][t], acc[mb][nb], 0, 0, 0);
     }
+    schedule_operand_reads<MB, NB>();
   };
   // Gated step: each X fragment read from LDS feeds both weights.
   auto mfma_step2 = [&](int cur, bf16x8 (&wb)[NB][4], bf16x8 (&wb2)[NB2][4]) {
@@ -254,6 +272,7 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
           acc2[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], wb2[nb][t], acc2[mb][nb], 0, 0, 0);
         }
     }
+    schedule_operand_reads<MB, 2 * NB>();
   };
 
   {
