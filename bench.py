@@ -169,6 +169,24 @@ def cpu_baseline(lin, x_bits, budget_s=12.0):
         passes += 1
     flops = 2.0 * rows * lin.n * lin.k * passes
     what = (f"{passes} passes over all {m_all} rows" if passes > 1 else f"{rows} of {m_all} rows")
+    one_thread = None
+    if lin.n * lin.k <= 5120 * 5120:
+        # the fp64 matmul alone on one BLAS thread, a row sample of a few seconds
+        try:
+            from threadpoolctl import threadpool_limits
+            wd = O.dequant(q, s)
+            r1, t1 = 1, 0.0
+            with threadpool_limits(limits=1):
+                while True:
+                    t0 = time.perf_counter()
+                    O.linear_exact(x_bits[:r1], wd)
+                    t1 = time.perf_counter() - t0
+                    if t1 * 2.5 > 3.0 or r1 >= m_all:
+                        break
+                    r1 = min(r1 * 2, m_all)
+            one_thread = {"tflops": 2.0 * r1 * lin.n * lin.k / t1 / 1e12, "rows": r1, "seconds": round(t1, 3)}
+        except Exception:  # pragma: no cover
+            one_thread = None
     return {
         "value": flops / total_t / 1e12,
         "unit": "TFLOP/s",
@@ -179,6 +197,7 @@ def cpu_baseline(lin, x_bits, budget_s=12.0):
         "cpu_model": cpu_model(),
         "dequant_s": round(split["dequant_s"], 3),
         "matmul_s": round(split["matmul_s"], 3),
+        "matmul_1thread": one_thread,
         "seconds": total_t,
         "rows": rows,
         "passes": passes,
