@@ -239,3 +239,89 @@ def test_w8a8_largest_k_sampled():
     mm, nn = np.meshgrid(ms, ns, indexing="ij")
     yr, ar = O.linear_w8a8_sampled(xq, xs, q, s, mm.ravel(), nn.ravel())
     assert_bound(y[mm.ravel(), nn.ravel()], yr, ar, "w8a8 largest K")
+
+
+# ---------------------------------------------------------------------------
+# activation quantizer: the quotient near E4M3 rounding midpoints
+# ---------------------------------------------------------------------------
+
+def _bf16_f32(bits16):
+    return (np.asarray(bits16, np.uint32) << 16).view(np.float32)
+
+
+def _groups(amax_bits, x_bits):
+    """Rows of one 1x128 group each: element 0 is the amax (+a), the other
+    127 are the given bf16 values (all |x| <= a), zero-padded."""
+    per = 127
+    rows = max(1, -(-len(x_bits) // per))
+    flat = np.zeros(rows * per, np.uint16)
+    flat[:len(x_bits)] = x_bits
+    out = np.empty((rows, 128), np.uint16)
+    out[:, 0] = amax_bits
+    out[:, 1:] = flat.reshape(rows, per)
+    return out
+
+
+def _near_midpoint_x(ab, count):
+    """The `count` positive bf16 x <= a whose IEEE quotient fl32(x / S) lies
+    closest (in ulps of the quotient) to a midpoint between E4M3 values: the
+    inputs where a quotient one ulp off would change the code."""
+    s = np.float32(_bf16_f32(ab)) / np.float32(448.0)
+    xb = np.arange(0, ab + 1, dtype=np.uint32)
+    q = (_bf16_f32(xb) / s).astype(np.float32).astype(np.float64)
+    tab = O.e4m3_table()[:0x7F]
+    mids = (tab[1:] + tab[:-1]) / 2.0
+    i = np.clip(np.searchsorted(mids, q), 1, len(mids) - 1)
+    d = np.minimum(np.abs(q - mids[i - 1]), np.abs(q - mids[i]))
+    d /= np.spacing(q.astype(np.float32)).astype(np.float64)
+    return xb[np.argsort(d, kind="stable")[:count]].astype(np.uint16)
+
+
+def test_act_quantize_near_midpoints():
+    """Codes of quotients within a few ulps of E4M3 midpoints, for amax over
+    the whole bf16 range, with every mantissa at the exponents where the
+    scale crosses 2^-64 (the kernel changes its division method there),
+    both signs, bit for bit against the oracle."""
+    rng = np.random.default_rng(47)
+    amax = [int(e << 7 | m) for e in range(0, 255, 3) for m in rng.integers(0, 128, 2)]
+    amax += [int(e << 7 | m) for e in (70, 71, 72, 73) for m in range(128)]   # a ~ 2^-57 .. 2^-54
+    amax = sorted({a for a in amax if 0 < a <= 0x7F7F})
+    rows = []
+    for ab in amax:
+        xb = _near_midpoint_x(ab, 200)
+        rows.append(_groups(ab, np.concatenate([xb, xb | np.uint16(0x8000)])))
+    x = np.concatenate(rows)
+    say("act quantize near midpoints", x.shape, len(amax), "amax values")
+    xq, xs = gpu_act_quantize(x)
+    exq, exs = O.act_quantize(x)
+    assert np.array_equal(xs.view(np.uint32), exs.view(np.uint32))
+    bad = np.argwhere(xq != exq)
+    assert bad.size == 0, [(hex(x[r, 0]), hex(x[r, c]), xq[r, c], exq[r, c]) for r, c in bad[:8]]
+
+
+@pytest.mark.skipif(__import__("os").environ.get("FP8BL_EXHAUSTIVE") != "1",
+                    reason="every (bf16 amax, bf16 x) pair, ~1e9 codes; set FP8BL_EXHAUSTIVE=1")
+def test_act_quantize_exhaustive_pairs():
+    """Every positive finite bf16 amax and every bf16 x with |x| <= amax,
+    both signs, through the GPU quantizer, bit for bit against the oracle."""
+    lo = 1
+    total = 0
+    while lo <= 0x7F7F:
+        hi, n = lo, 0
+        while hi <= 0x7F7F and n < 24_000_000:
+            n += 2 * (hi + 1)
+            hi += 1
+        rows = []
+        for ab in range(lo, hi):
+            xb = np.arange(0, ab + 1, dtype=np.uint16)
+            rows.append(_groups(ab, np.concatenate([xb, xb | np.uint16(0x8000)])))
+        x = np.concatenate(rows)
+        say("act quantize exhaustive amax", hex(lo), "..", hex(hi - 1), x.shape)
+        xq, xs = gpu_act_quantize(x)
+        exq, exs = O.act_quantize(x)
+        assert np.array_equal(xs.view(np.uint32), exs.view(np.uint32))
+        bad = np.argwhere(xq != exq)
+        assert bad.size == 0, [(hex(x[r, 0]), hex(x[r, c]), xq[r, c], exq[r, c]) for r, c in bad[:8]]
+        total += x.size
+        lo = hi
+    say("act quantize exhaustive codes checked", total)
