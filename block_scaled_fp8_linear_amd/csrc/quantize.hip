@@ -6,9 +6,9 @@
 //   amax = max |w|;  S = fl32(amax / 448), or 1 when amax == 0;
 //   code = nearest finite E4M3 to fl32(w / S), ties to the even code,
 //          saturating at 448, sign kept.
-// One workgroup per block; offline work, so it favours exactness over speed
-// (two IEEE divisions per element). The input is fp32, or bf16 widened
-// exactly to fp32 (a checkpoint stored in bf16).
+// One workgroup per block; offline work, so every element takes an IEEE
+// division. The input is fp32, or bf16 widened exactly to fp32 (a
+// checkpoint stored in bf16).
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
@@ -16,30 +16,19 @@ namespace fp8bl {
 
 namespace {
 
-// Nearest E4M3FN code to a finite fp32 value (ties to even, saturating).
-// Normal range (|v| >= 2^-6): round the 23-bit fp32 mantissa to 3 bits by
-// adding half an E4M3 ulp minus one plus the kept lsb, then rebias the
-// exponent from 127 to 7 (the carry of a round-up walks into the exponent,
-// which is exactly the next code). Subnormal range: |v| * 2^9 is exact and
-// rintf rounds it to the nearest integer, ties to even; 8 becomes the
-// smallest normal code 0x08 by construction.
-__device__ __forceinline__ uint32_t e4m3_from_f32(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {                 // |v| >= 448
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {           // |v| < 2^-6
-    code = (uint32_t)rintf(__builtin_bit_cast(float, a) * 512.0f);
-  } else {
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  }
-  return code | sign;
-}
-
 constexpr int kThreads = 256;
+
+// Two fp32 values -> their E4M3FN codes in bytes 0 and 1 (HI false) or 2
+// and 3 (HI) of `old`, by the gfx950 conversion v_cvt_pk_fp8_f32: nearest
+// code, ties to even, sign kept (-0 -> 0x80). Over every fp32 pattern below
+// 464 in magnitude, both signs, it gives the same codes as an integer
+// nearest-even encoder that saturates at 448 (checked exhaustively on
+// MI355X). The quotients w / S and x / S of both quantizers stay below
+// 448 * (1 + 2^-23), where saturation and rounding to 448 coincide.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_hw(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
 
 // Four consecutive inputs as fp32: fp32 loads as they are; bf16 widens
 // exactly (its 16 bits are the high half of the fp32 pattern).
@@ -93,23 +82,11 @@ void quantize_kernel(const T* __restrict__ w, uint8_t* __restrict__ q,
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const f32x4 t = v[c4 * 4 + d];
-      out[d] = e4m3_from_f32(__fdiv_rn(t[0], sc)) |
-               (e4m3_from_f32(__fdiv_rn(t[1], sc)) << 8) |
-               (e4m3_from_f32(__fdiv_rn(t[2], sc)) << 16) |
-               (e4m3_from_f32(__fdiv_rn(t[3], sc)) << 24);
+      out[d] = e4m3x2_hw<true>(__fdiv_rn(t[2], sc), __fdiv_rn(t[3], sc),
+                               e4m3x2_hw<false>(__fdiv_rn(t[0], sc), __fdiv_rn(t[1], sc), 0u));
     }
     *reinterpret_cast<u32x4*>(q + (size_t)row * K + col) = out;
   }
-}
-
-// Two fp32 values -> their E4M3 codes in bytes 0 and 1 (`hi` false) or 2
-// and 3 (HI) of `old`, by the hardware conversion (round to nearest even). Over
-// every fp32 pattern below 464 in magnitude, both signs, it gives the codes
-// of e4m3_from_f32 (checked exhaustively on MI355X); quotients here stay
-// below 448 * (1 + 2^-23).
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_hw(float a, float b, uint32_t old) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
 // Activation quantizer of the W8A8 route: per token, per 1x128 K group,

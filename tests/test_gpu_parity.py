@@ -163,6 +163,36 @@ def test_quantize_subnormal_and_tie_values():
     assert np.array_equal(u8(qt), q)
 
 
+def test_quantize_codes_around_every_midpoint():
+    """With S = 1 (a block holding 448) the codes are the E4M3 encoding of
+    the fp32 inputs themselves: every midpoint between neighbouring codes and
+    the 8 fp32 values on each side of it, both signs, plus every code value
+    and its fp32 neighbours, bit for bit against the oracle."""
+    t = O.e4m3_table()[:0x7F]
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([mids, t.astype(np.float32)])
+    bits_ = pts.view(np.uint32).astype(np.int64)
+    near = np.concatenate([bits_ + d for d in range(-8, 9)])
+    near = near[(near >= 0) & (near < 0x80000000)].astype(np.uint32).view(np.float32)
+    near = near[np.isfinite(near) & (np.abs(near) <= 448.0)]
+    vals = np.concatenate([near, -near, [0.0, -0.0]]).astype(np.float32)
+    rows = -(-vals.size // 254)
+    flat = np.zeros(rows * 254, dtype=np.float32)
+    flat[:vals.size] = vals
+    flat = flat.reshape(rows, 254)
+    w = np.zeros((rows, 256), dtype=np.float32)
+    w[:, 0] = w[:, 128] = 448.0                    # both column blocks hold amax 448 -> S = 1
+    w[:, 1:128], w[:, 129:] = flat[:, :127], flat[:, 127:]
+    say("quantize around midpoints", w.shape)
+    qt, st = F.fp8_block_quantize(to_f32(w))
+    torch.cuda.synchronize()
+    q, s = O.quantize(w)
+    assert np.all(s == 1.0)
+    assert np.array_equal(f32(st).view(np.uint32), s.view(np.uint32))
+    bad = np.argwhere(u8(qt) != q)
+    assert bad.size == 0, [(float(w[r, c]), int(u8(qt)[r, c]), int(q[r, c])) for r, c in bad[:8]]
+
+
 # ---------------------------------------------------------------------------
 # linear: bound against the fp64 oracle, both kernels forced on small shapes
 # ---------------------------------------------------------------------------
