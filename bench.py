@@ -73,6 +73,7 @@ KERNEL_SOURCES = {
     "quantize_kernel": ("quantize.hip",),
     "act_quantize_kernel": ("quantize.hip",),
     "gemm_w8a8_kernel": ("gemm_w8a8.hip",),
+    "stream_read_kernel": ("stream_read.hip",),
 }
 SHARED_SOURCES = ("fp8bl_api.hip", "fp8bl_device.h", "fp8bl_internal.h")
 
@@ -215,25 +216,49 @@ def cpu_model():
 
 
 def stream_ceiling(nbytes=1 << 30, reps=10):
-    """A plain library streaming read (torch's sum over a large bf16 tensor)
-    and copy on the device: the practical HBM ceilings the HBM-bound kernels
-    are compared with."""
+    """Practical HBM ceilings the HBM-bound kernels are compared with: the
+    library's plain streaming read (fp8_block_stream_read) over 8 rotated
+    copies of a buffer the size of the skinny workload's weight (524 MB in
+    all, twice the MALL) and over one 1 GiB buffer, plus torch's sum (a
+    read with a reduction) and copy over 1 GiB."""
     import torch
-    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
-    y = torch.empty_like(x)
-    for _ in range(3):
-        x.sum(); y.copy_(x)
-    torch.cuda.synchronize()
+    from block_scaled_fp8_linear_amd import _lib
+    dev = torch.device("cuda:0")
     out = {}
-    for name, fn, moved in (("torch_sum_read", lambda: x.sum(), nbytes), ("torch_copy", lambda: y.copy_(x), 2 * nbytes)):
+    blocks = 2048
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            fn()
+        for i in range(n):
+            fn(i)
         e1.record()
         torch.cuda.synchronize()
-        out[name + "_GBps"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    def read(buf):
+        st = torch.cuda.current_stream().cuda_stream
+        rc = _lib.stream_read_raw(buf.data_ptr(), buf.numel(), sink.data_ptr(), blocks, st)
+        if rc != 0:
+            raise RuntimeError(_lib.status_string(rc))
+
+    wbytes = 8000 * 8192
+    bufs = [torch.ones(wbytes, dtype=torch.uint8, device=dev) for _ in range(8)]
+    t = timed(lambda i: read(bufs[i % 8]), 40)
+    out["stream_read_66MB_GBps"] = round(wbytes / t / 1e9, 1)
+    del bufs
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    xb = x.view(torch.uint8)
+    t = timed(lambda i: read(xb), reps)
+    out["stream_read_1GiB_GBps"] = round(nbytes / t / 1e9, 1)
+    y = torch.empty_like(x)
+    out["torch_sum_read_GBps"] = round(nbytes / timed(lambda i: x.sum(), reps) / 1e9, 1)
+    out["torch_copy_GBps"] = round(2 * nbytes / timed(lambda i: y.copy_(x), reps) / 1e9, 1)
     return out
 
 
@@ -257,7 +282,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--stream-ceiling", action="store_true",
-                    help="only time a plain 1 GiB streaming read and copy (practical HBM ceilings) and exit")
+                    help="only time plain streaming reads and a copy (practical HBM ceilings) and exit")
     args = ap.parse_args()
 
     if args.copy_calibration:

@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_quantize.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fp8_block_quantize_bf16.restype = c_int
     lib.fp8_block_quantize_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.fp8_block_stream_read.restype = c_int
+    lib.fp8_block_stream_read.argtypes = [vp, sz, vp, c_int, vp]
     _lib = lib
     return lib
 
@@ -141,3 +143,7 @@ def quantize_raw(w: int, q: int, s: int, n: int, k: int, stream: int = 0) -> int
 
 def quantize_bf16_raw(w: int, q: int, s: int, n: int, k: int, stream: int = 0) -> int:
     return load().fp8_block_quantize_bf16(w, q, s, n, k, stream)
+
+
+def stream_read_raw(buf: int, nbytes: int, sink: int, blocks: int, stream: int = 0) -> int:
+    return load().fp8_block_stream_read(buf, nbytes, sink, blocks, stream)

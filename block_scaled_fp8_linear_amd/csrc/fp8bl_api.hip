@@ -314,3 +314,14 @@ FP8BL_EXPORT int fp8_block_quantize_bf16(const uint16_t* w_bf16, uint8_t* q, flo
   if (st != FP8BL_OK) return st;
   return hip_status(fp8bl::launch_quantize_bf16(w_bf16, q, scale_inv, n, k, stream));
 }
+
+FP8BL_EXPORT int fp8_block_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                                       hipStream_t stream) {
+  if (bytes == 0) return FP8BL_OK;
+  if (!buf || !sink || blocks < 1 || blocks > 65536 || (bytes % 16) != 0) return FP8BL_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return FP8BL_ALIGNMENT;
+  if (overlap(sink, (size_t)blocks * 256 * 4, buf, bytes)) return FP8BL_INVALID_ARG;
+  const int st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  return hip_status(fp8bl::launch_stream_read(buf, bytes, sink, blocks, stream));
+}

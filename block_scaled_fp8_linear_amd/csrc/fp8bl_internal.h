@@ -47,6 +47,11 @@ hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* 
 hipError_t launch_reduce_partials(const float* part, uint16_t* y, int splits,
                                   int64_t m, int64_t n, hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 16) by `blocks` workgroups of 256
+// threads; one XOR-folded word per thread into sink[blocks * 256].
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t stream);
+
 constexpr size_t kWorkspaceAlign = 256;
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Split-K partial slabs ([M,N] fp32 each) start every 64 floats, so every

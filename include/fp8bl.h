@@ -197,6 +197,19 @@ int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,
 int fp8_block_quantize_bf16(const uint16_t* w_bf16, uint8_t* q, float* scale_inv,
                             int64_t n, int64_t k, hipStream_t stream);
 
+/* Measurement aid, not part of the layer: a plain streaming read of `bytes`
+ * of device memory (16-byte non-temporal loads, grid-stride, `blocks`
+ * workgroups of 256 threads), the practical HBM ceiling for the
+ * bandwidth-bound kernels. Each thread writes the XOR of the 32-bit words it
+ * read to sink[block * 256 + thread], so the XOR over the whole sink equals
+ * the XOR of every word of the buffer.
+ *   buf     device memory (in, 16-B aligned), bytes % 16 == 0
+ *   sink    [blocks * 256] uint32 (out, 4-B aligned, not overlapping buf)
+ *   blocks  1 .. 65536
+ * bytes == 0 is a no-op. */
+int fp8_block_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

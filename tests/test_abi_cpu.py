@@ -21,7 +21,7 @@ def test_header_symbols_exported(lib):
         "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
         "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
         "fp8_block_mlp_gate_up", "fp8_act_quantize", "fp8_block_linear_w8a8_workspace_size",
-        "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16",
+        "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16", "fp8_block_stream_read",
     }
     for name in names:
         assert hasattr(lib, name), name
@@ -193,3 +193,19 @@ def test_element_count_limit_is_strict(lib):
     assert L.dequant_raw(FAKE, 8 * FAKE, 16 * FAKE, n, k) == L.FP8BL_INVALID_ARG
     assert L.quantize_raw(FAKE, 8 * FAKE, 16 * FAKE, n, k) == L.FP8BL_INVALID_ARG
     assert L.act_quantize_raw(FAKE, 8 * FAKE, 16 * FAKE, n, k) == L.FP8BL_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    # (buf, bytes, sink, blocks)
+    ((FAKE, 0, 0, 0), L.FP8BL_OK),                          # empty read: no-op
+    ((0, 1 << 20, 64 * FAKE, 2048), L.FP8BL_INVALID_ARG),     # null buffer
+    ((FAKE, 1 << 20, 0, 2048), L.FP8BL_INVALID_ARG),          # null sink
+    ((FAKE, 1 << 20, 64 * FAKE, 0), L.FP8BL_INVALID_ARG),     # no workgroups
+    ((FAKE, 1 << 20, 64 * FAKE, 65537), L.FP8BL_INVALID_ARG),
+    ((FAKE, (1 << 20) + 8, 64 * FAKE, 2048), L.FP8BL_INVALID_ARG),   # not a multiple of 16
+    ((FAKE + 8, 1 << 20, 64 * FAKE, 2048), L.FP8BL_ALIGNMENT),
+    ((FAKE, 1 << 20, 64 * FAKE + 2, 2048), L.FP8BL_ALIGNMENT),
+    ((FAKE, 1 << 20, FAKE + 4096, 2048), L.FP8BL_INVALID_ARG),       # sink inside the buffer
+])
+def test_stream_read_argument_errors(lib, args, status):
+    assert L.stream_read_raw(*args) == status
