@@ -30,18 +30,21 @@
 // Split-K over K blocks (gridDim.y > 1) writes fp32 partial tiles that the
 // ordered reduce kernel sums, as in the bf16 path.
 //
-// Measured on MI355X (16384x3072x3072): the step is bound by LDS bandwidth.
-// Per workgroup step the four waves read 16 KB each of A and B fragments
-// and the tile is staged with 32 KB of writes: at full MFMA rate that is as
-// many LDS cycles as MFMA cycles. The same kernel without its global loads
+// Measured on MI355X (16384x3072x3072): no single resource bounds the
+// step. At the full MFMA rate its LDS traffic (16 KB of A and B fragments
+// per wave and 32 KB of staging writes per workgroup and step) would keep
+// the LDS as busy as the matrix core; the counters show the matrix core
+// busy about a third of the time. The same kernel without its global loads
 // runs within 20% of the full one, without its MFMAs within 18%, while the
-// global -> LDS staging alone takes 14% of the time. Tried and slower or no
-// faster: B fragments loaded from memory straight into registers (1.6x
-// slower: 16-row x 64-byte loads), 256x128 tiles with 8 waves and a
-// three-stage direct-to-LDS ring, the weight scale loaded one step ahead
-// with the operand reads in first-use order. Larger per-wave tiles (fewer
-// LDS bytes per MFMA) are what would move it, at a register cost that
-// leaves one workgroup per CU.
+// global -> LDS staging alone takes 14% of the time: a chain of latencies
+// per step rather than one bound. Tried and slower or no faster: B fragments
+// loaded from memory straight into registers (1.6x slower: 16-row x 64-byte
+// loads), 256x128 tiles with 8 waves and a three-stage direct-to-LDS ring,
+// the weight scale loaded one step ahead with the operand reads in
+// first-use order, the staging loads issued two steps ahead through a second
+// register set (2-7% slower). Larger per-wave tiles (fewer LDS bytes per
+// MFMA) would shorten the chain, at a register cost that leaves one
+// workgroup per CU.
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
