@@ -222,7 +222,7 @@ def stream_ceiling(nbytes=1 << 30, reps=10):
     all, twice the MALL) and over one 1 GiB buffer, plus torch's sum (a
     read with a reduction) and copy over 1 GiB."""
     import torch
-    from block_scaled_fp8_linear_amd import _lib
+    import block_scaled_fp8_linear_amd as F
     dev = torch.device("cuda:0")
     out = {}
     blocks = 2048
@@ -242,10 +242,7 @@ def stream_ceiling(nbytes=1 << 30, reps=10):
         return e0.elapsed_time(e1) / 1e3 / n
 
     def read(buf):
-        st = torch.cuda.current_stream().cuda_stream
-        rc = _lib.stream_read_raw(buf.data_ptr(), buf.numel(), sink.data_ptr(), blocks, st)
-        if rc != 0:
-            raise RuntimeError(_lib.status_string(rc))
+        F.fp8_block_stream_read(buf, blocks, sink)
 
     wbytes = 8000 * 8192
     bufs = [torch.ones(wbytes, dtype=torch.uint8, device=dev) for _ in range(8)]

@@ -14,6 +14,8 @@ hand-written HIP) provides:
 * ``fp8_act_quantize(x)`` -> (xq, x_scale)  per-token 1x128 activation quantizer
 * ``fp8_block_linear_w8a8(xq, x_scale, q, s)`` / ``fp8_block_linear_w8a8_bf16(x, q, s)``
   -> bf16 Y from E4M3 x E4M3 products on the FP8 matrix cores (W8A8 route)
+* ``fp8_block_stream_read(buf)`` -> a plain streaming read of device memory
+  (measurement aid: the practical HBM ceiling)
 
 ``block_scaled_fp8_linear_amd.checkpoint`` converts a state dict into the
 serialized block-FP8 checkpoint (quantization on the GPU, safetensors shards,
@@ -42,7 +44,7 @@ __all__ = [
     "fp8_act_quantize", "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16",
     "workspace_size", "w8a8_workspace_size",
     "device_supported", "abi_version", "status_string", "Fp8blError",
-    "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "scale_grid_shape",
+    "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "scale_grid_shape", "fp8_block_stream_read",
 ]
 
 
@@ -258,3 +260,22 @@ def fp8_block_linear_w8a8_bf16(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor
                                          m, n, k, ws_ptr, ws_bytes, _stream(x.device)),
                "fp8_block_linear_w8a8_bf16")
     return out
+
+
+def fp8_block_stream_read(buf: torch.Tensor, blocks: int = 2048,
+                          sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement aid: a plain streaming read of a contiguous device tensor
+    (its byte size a multiple of 16) by ``blocks`` workgroups; returns the
+    int32 sink [blocks * 256] whose XOR is the XOR of the tensor's words."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    _need(sink, torch.int32, "sink")
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink must hold blocks * 256 words")
+    nbytes = buf.numel() * buf.element_size()
+    with torch.cuda.device(buf.device):
+        _check(_lib.stream_read_raw(buf.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                                    _stream(buf.device)), "fp8_block_stream_read")
+    return sink

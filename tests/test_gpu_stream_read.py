@@ -31,3 +31,15 @@ def test_stream_read_xor(nbytes, blocks):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+def test_stream_read_binding():
+    """The torch-level wrapper: same sink XOR, and a sink too small raises."""
+    import block_scaled_fp8_linear_amd as F
+    buf = torch.arange(1 << 16, dtype=torch.int32, device="cuda:0")
+    sink = F.fp8_block_stream_read(buf, blocks=5)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == \
+        np.bitwise_xor.reduce(np.arange(1 << 16, dtype=np.uint32))
+    with pytest.raises(ValueError):
+        F.fp8_block_stream_read(buf, blocks=5, sink=torch.empty(8, dtype=torch.int32, device="cuda:0"))
