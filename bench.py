@@ -78,11 +78,40 @@ KERNEL_SOURCES = {
 SHARED_SOURCES = ("fp8bl_api.hip", "fp8bl_device.h", "fp8bl_internal.h")
 
 
+def code_only(src):
+    """C++ source bytes without ``//`` and ``/* */`` comments, trailing blanks
+    or empty lines; string and character literals are kept as written. An
+    edit to comments alone therefore leaves the hash below unchanged."""
+    s = src.decode("utf-8", "surrogateescape")
+    out, i, n = [], 0, len(s)
+    while i < n:
+        c = s[i]
+        if s.startswith("//", i):
+            j = s.find("\n", i)
+            i = n if j < 0 else j
+        elif s.startswith("/*", i):
+            j = s.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and s[j] != c:
+                j += 2 if s[j] == "\\" else 1
+            out.append(s[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line).encode("utf-8", "surrogateescape")
+
+
 def kernel_source_sha(kernels=None, read=None):
-    """Hash of the HIP sources of ``kernels`` (names as rocprofv3 prints them,
-    template arguments allowed) plus the shared device and launch files; all
-    of csrc when ``kernels`` is None. ``read(name) -> bytes`` supplies file
-    contents (default: the working tree)."""
+    """Hash of the code (comments excluded, see ``code_only``) of the HIP
+    sources of ``kernels`` (names as rocprofv3 prints them, template arguments
+    allowed) plus the shared device and launch files; all of csrc when
+    ``kernels`` is None. ``read(name) -> bytes`` supplies file contents
+    (default: the working tree)."""
     import glob
     import hashlib
     csrc = os.path.join(ROOT, "block_scaled_fp8_linear_amd", "csrc")
@@ -101,7 +130,7 @@ def kernel_source_sha(kernels=None, read=None):
     h = hashlib.sha256()
     for name in names:
         h.update(name.encode())
-        h.update(read(name))
+        h.update(code_only(read(name)))
     return h.hexdigest()[:16]
 
 

@@ -1,9 +1,10 @@
 // Standalone block dequant: Q[N,K] E4M3 + S[GN,GK] fp32 -> bf16 W_hat[N,K].
 //
-// FastVideo PR #1829, "Purpose": the block-scaled weight is dequantized to
-// BF16 right before a plain matmul (the transient weight of the Hopper route,
-// "Checklist": at most ~0.26 GB for the largest layer). "Changes", tests
-// bullet: bit-exact against the reference broadcast.
+// FastVideo PR #1829, "Purpose": the Hopper route turns each block-scaled
+// weight into BF16 just ahead of the layer's matmul ("Checklist": that
+// temporary BF16 copy reaches about 0.26 GB for the biggest layer).
+// "Changes", tests bullet: the output must match, bit for bit, decoding the
+// codes and multiplying by the scale grid expanded over its blocks.
 //
 // HBM-bound: 1 byte read and 2 bytes written per element (+ the scale grid,
 // which stays in cache). Each thread moves 8-code chunks (8 bytes in, 16

@@ -2,8 +2,8 @@
 // bytes of the E4M3 weight, so the kernel is organised around streaming W
 // once, at full bandwidth, with as many 16-byte loads in flight as possible.
 //
-// Same arithmetic as the tiled path (FastVideo PR #1829, "Purpose":
-// dequantize to BF16 then a plain matmul; fp32 accumulation, one bf16
+// Same arithmetic as the tiled path (FastVideo PR #1829, "Purpose": the
+// weight goes to BF16, then an ordinary matmul; fp32 accumulation, one bf16
 // rounding per output).
 //
 // Work unit: a workgroup of W waves owns 16*NT weight rows and one K range

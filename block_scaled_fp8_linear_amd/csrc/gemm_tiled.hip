@@ -1,11 +1,12 @@
 // Fused block-FP8 linear for large M: Y[M,N] = X[M,K] * W_hat[N,K]^T.
 //
-// FastVideo PR #1829, "Purpose": each linear dequantizes its block-scaled
-// weight to BF16 right before a plain matmul. Here the BF16 weight never
-// reaches memory: E4M3 codes go from HBM straight into the registers of the
-// wave that consumes them, are dequantized there (fp32 multiply by the
-// block's weight_scale_inv, RNE to bf16) and fed to bf16 MFMA with fp32
-// accumulators (LightX2V PR #1657, "Walkthrough": FP32 accumulation).
+// FastVideo PR #1829, "Purpose": the Hopper route converts every layer's
+// block-scaled weight to BF16 just ahead of an ordinary matmul. Here the
+// BF16 weight never reaches memory: E4M3 codes go from HBM straight into
+// the registers of the wave that consumes them, are dequantized there (fp32
+// multiply by the block's weight_scale_inv, RNE to bf16) and fed to bf16
+// MFMA with fp32 accumulators (LightX2V PR #1657, "Walkthrough": FP32
+// accumulation).
 //
 // Workgroup tile BM x BN, 4 waves side by side along N: wave w owns the
 // BN/4 weight rows [n0 + w*BN/4, ...) for all BM rows of X. Every weight

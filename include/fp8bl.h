@@ -74,9 +74,10 @@ const char* fp8_block_status_string(int status);
  * gfx950, else 0 (also 0 when the device cannot be queried). Host only. */
 int fp8_block_device_supported(int device);
 
-/* Standalone dequant (FastVideo PR #1829, "Purpose": the block-scaled weight
- * is dequantized to BF16 before a plain matmul; "Changes", tests bullet: the
- * result is bit-exact against the reference broadcast).
+/* Standalone dequant (FastVideo PR #1829, "Purpose": the Hopper route turns
+ * the block-scaled weight into BF16 ahead of the matmul; "Changes", tests
+ * bullet: the result must equal, bit for bit, the decoded codes times the
+ * scale grid expanded over its blocks).
  *   q          [n,k] E4M3 bytes          (in, 16-B aligned)
  *   scale_inv  [ceil(n/128),ceil(k/128)] fp32 (in, 4-B aligned)
  *   w_bf16     [n,k] bf16 bits           (out, 16-B aligned, may not overlap)
@@ -88,8 +89,8 @@ int fp8_block_dequant(const uint8_t* q, const float* scale_inv, uint16_t* w_bf16
  * this shape with ANY path (0 when none). Host only; never fails. */
 size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_t k);
 
-/* The linear layer (FastVideo PR #1829, "Purpose": dequantize to BF16, then a
- * plain matmul; LightX2V PR #1657, "Walkthrough": FP32 accumulation):
+/* The linear layer (FastVideo PR #1829, "Purpose": the weight goes to BF16,
+ * then an ordinary matmul; LightX2V PR #1657, "Walkthrough": FP32 accumulation):
  *   y[m,n] = bf16_rne( sum_k x[m,k] * What[n,k] ),  What as in fp8_block_dequant,
  * with fp32 accumulation and one bf16 rounding per output. What is formed in
  * registers only. No bias. K may be at most 2^20.

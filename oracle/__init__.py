@@ -10,12 +10,13 @@ Sources (page titles and sections, not line numbers):
 
 * FastVideo PR #1829, "[feat] MiniMax H3: block-FP8 text encoder on Hopper, its
   converter, and a 4xH100 FastH3 profile":
-    - "Purpose": each linear dequantizes its block-scaled weight to BF16 right
-      before a plain matmul.
+    - "Purpose": the Hopper route converts each layer's block-scaled weight
+      to BF16 just ahead of an ordinary matmul.
     - "Changes", converter bullet: E4M3 weight plus a [N/128, K/128]
       ``weight_scale_inv`` grid.
-    - "Changes", tests bullet: the dequantizer is bit-exact against the
-      reference broadcast, and the FP8 round trip stays within E4M3 precision.
+    - "Changes", tests bullet: the dequantizer must equal, bit for bit, a
+      decode multiplied by the scale grid expanded over its blocks, and
+      quantizing then dequantizing must lose no more than E4M3 resolution.
 * LightX2V PR #1657, "Walkthrough": FP8 GEMM with FP32 accumulation.
 * FastVideo PR #1829, "Changes", first bullet: the Blackwell route also
   needs a Triton quantizer beside the FlashInfer groupwise GEMM; read here as

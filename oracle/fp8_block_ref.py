@@ -118,8 +118,8 @@ def bf16_rne_bits_nearest(x32: np.ndarray) -> np.ndarray:
 # Block dequant.  FastVideo PR #1829, "Purpose" and "Changes":
 #   W_hat[n,k] = bf16( fl32( e4m3(Q[n,k]) * S[n//128, k//128] ) )
 # The scale grid is expanded over its blocks and trimmed to [N,K] (the
-# "reference broadcast"), multiplied in fp32, then rounded to bf16: two
-# roundings, in that order.
+# broadcast form the tests bullet compares against), multiplied in fp32,
+# then rounded to bf16: two roundings, in that order.
 # ---------------------------------------------------------------------------
 
 def scale_grid_shape(n: int, k: int) -> tuple[int, int]:
@@ -235,8 +235,8 @@ def quantize_bf16(w_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 
 
 # ---------------------------------------------------------------------------
-# Linear.  FastVideo PR #1829, "Purpose": a plain matmul of the dequantized
-# bf16 weight, Y = X W_hat^T; LightX2V PR #1657 "Walkthrough": accumulation in
+# Linear.  FastVideo PR #1829, "Purpose": an ordinary matmul with the
+# dequantized bf16 weight, Y = X W_hat^T; LightX2V PR #1657 "Walkthrough": accumulation in
 # FP32 (the GPU side). The oracle forms the exact-arithmetic target in fp64
 # and grades against it with the stated bound
 #   |y - Y*| <= 2^-7 |Y*| + 1e-4 * sum_k |x_k w_k|.

@@ -23,7 +23,7 @@ def test_every_csrc_kernel_file_is_mapped():
 
 def test_source_sha_depends_only_on_the_kernels_files():
     real = lambda name: open(os.path.join(ROOT, "block_scaled_fp8_linear_amd", "csrc", name), "rb").read()
-    edited = lambda name: real(name) + (b"// edit\n" if name == "gemm_w8a8.hip" else b"")
+    edited = lambda name: real(name) + (b"static int edit_marker;\n" if name == "gemm_w8a8.hip" else b"")
     tiled = ["gemm_tiled_kernel<128, 128, 2>", "reduce_partials_kernel"]
     w8 = ["gemm_w8a8_kernel", "act_quantize_kernel"]
     assert bench.kernel_source_sha(tiled, read=real) == bench.kernel_source_sha(tiled, read=edited)
@@ -33,6 +33,32 @@ def test_source_sha_depends_only_on_the_kernels_files():
         bench.kernel_source_sha(["gemm_tiled_kernel<128, 256, 2>"], read=real)
     with pytest.raises(KeyError):
         bench.kernel_source_sha(["some_other_kernel"], read=real)
+
+
+def test_source_sha_ignores_comments_only():
+    real = lambda name: open(os.path.join(ROOT, "block_scaled_fp8_linear_amd", "csrc", name), "rb").read()
+    tiled = ["gemm_tiled_kernel<128, 128, 2>"]
+    base = bench.kernel_source_sha(tiled, read=real)
+
+    def commented(name):
+        src = real(name)
+        if name != "gemm_tiled.hip":
+            return src
+        # a new comment line, a reworded block comment, a trailing comment
+        return (b"// note\n" + src.replace(b"namespace fp8bl {", b"namespace fp8bl {  /* x */", 1)
+                + b"\n\n// end\n")
+
+    def recoded(name):
+        src = real(name)
+        return src.replace(b"constexpr int kBK = 64;", b"constexpr int kBK = 32;", 1) \
+            if name == "gemm_tiled.hip" else src
+
+    assert b"constexpr int kBK = 64;" in real("gemm_tiled.hip")
+    assert bench.kernel_source_sha(tiled, read=commented) == base
+    assert bench.kernel_source_sha(tiled, read=recoded) != base
+    # comment markers inside literals are code
+    assert bench.code_only(b'const char* s = "// x";\n') == b'const char* s = "// x";'
+    assert bench.code_only(b"char c = '/'; // y\nint z;\n") == b"char c = '/';\nint z;"
 
 
 def test_measured_traffic_follows_the_recorded_sha(tmp_path, monkeypatch):

@@ -234,7 +234,7 @@ def test_dequant_power_of_two_scales_are_exact_and_follow_blocks():
 
 
 def test_dequant_matches_torch_reference_broadcast():
-    """The "reference broadcast" read literally: decode with the library's
+    """The broadcast comparison taken literally: decode with the library's
     float8_e4m3fn, expand the scale grid, multiply in fp32, cast to bf16."""
     torch = pytest.importorskip("torch")
     wl = generate("tiny")
