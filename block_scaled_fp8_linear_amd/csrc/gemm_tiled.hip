@@ -8,8 +8,9 @@
 // MFMA with fp32 accumulators (LightX2V PR #1657, "Walkthrough": FP32
 // accumulation).
 //
-// Workgroup tile BM x BN, 4 waves side by side along N: wave w owns the
-// BN/4 weight rows [n0 + w*BN/4, ...) for all BM rows of X. Every weight
+// Workgroup tile BM x BN, W waves side by side along N: wave w owns the
+// BN/W weight rows [n0 + w*BN/W, ...) for all BM rows of X (W = 4, or 8 for
+// the 128x256 tile, where each wave keeps one 32-column block). Every weight
 // element is therefore decoded exactly once per workgroup (decode VALU per
 // MFMA flop falls as 1/BM), while the X tile is shared through LDS, staged
 // with 16-byte loads into an XOR-swizzled layout that the MFMA operand reads
@@ -22,9 +23,15 @@
 // runs step k's MFMAs from LDS and the decoded registers, then stages X for
 // step k+1 into the other LDS buffer. Two or three workgroups share each CU
 // (three with 128x128 tiles), so one workgroup's decode overlaps another's
-// MFMAs. Loads go through buffer
-// descriptors covering only the tile's valid rows: rows past M or N and the
-// K tail read as zero without branches. (Measured alternatives that did not
+// MFMAs. The 128x256 tile runs 8 waves of one 32-column block each (about
+// 130 VGPRs, two workgroups per CU): per 128x128x64 step of work it moves
+// 16 KB of X and codes through the CU's vector-memory path against 24 KB
+// for two 128x128 workgroups, which measured 2-6% faster than both the
+// 4-wave 128x256 tile and 128x128 on the shapes that choose it (the load
+// path of a CU, not the matrix core, limits these kernels: the time to
+// issue a step's loads grows with the workgroups sharing the CU). Loads go
+// through buffer descriptors covering only the tile's valid rows: rows past
+// M or N and the K tail read as zero without branches. (Measured alternatives that did not
 // pay on MI355X: decoding step k+1 inside step k's MFMA stream with two
 // operand sets, and prefetching two steps ahead.)
 //
@@ -109,17 +116,18 @@ __device__ __forceinline__ void schedule_operand_reads() {
 // GATED: the MLP gate/up pair in one pass. The same X tile feeds two weights
 // (q, s = gate; q2, s2 = up) into two accumulator sets and the epilogue
 // writes swiglu(gate, up) instead of either product.
-template <int BM, int BN, bool GATED>
+template <int BM, int BN, bool GATED, int WAVES>
 __device__ __forceinline__
 void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                 const float* __restrict__ s, uint16_t* __restrict__ y,
                 float* __restrict__ part, int M, int N, int K, int gk,
                 int tiles_m, int tiles_n, int kt_per_split,
                 const uint8_t* __restrict__ q2, const float* __restrict__ s2) {
-  constexpr int WN = BN / 4;            // weight rows per wave
+  constexpr int kT = WAVES * 64;        // threads
+  constexpr int WN = BN / WAVES;        // weight rows per wave
   constexpr int NB = WN / 32;           // 32-wide MFMA column blocks per wave
   constexpr int MB = BM / 32;           // 32-tall MFMA row blocks
-  constexpr int XCH = BM * kBK / 8 / kThreads;  // 16-byte X chunks per thread per step
+  constexpr int XCH = BM * kBK / 8 / kT;  // 16-byte X chunks per thread per step
   static_assert(WN % 32 == 0 && 128 % WN == 0, "wave rows must sit in one scale block");
   static_assert(XCH >= 1, "tile too small");
 
@@ -150,13 +158,13 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   const int kt0 = blockIdx.y * kt_per_split;
   const int kt1 = min(kt0 + kt_per_split, nkt);
 
-  // ---- X: thread moves chunk (tid & 7) of tile rows (tid >> 3) + 32 i.
+  // ---- X: thread moves chunk (tid & 7) of tile rows (tid >> 3) + (kT / 8) i.
   const __amdgpu_buffer_rsrc_t xrs =
       make_rsrc(x + (size_t)m0 * K, (uint32_t)(min(M - m0, BM) * K * 2));
   const int xc = tid & 7;
   const int xr0 = tid >> 3;
   const uint32_t xoff0 = (uint32_t)(xr0 * K * 2 + xc * 16);
-  const uint32_t xrow_stride = (uint32_t)(32 * K * 2);
+  const uint32_t xrow_stride = (uint32_t)((kT / 8) * K * 2);
 
   // ---- W codes: lane holds 16 codes of row (lane % 32) of each column
   // block, k chunk (lane / 32) of each 32-wide k slab.
@@ -181,7 +189,7 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
-      *reinterpret_cast<u32x4*>(&xs[buf][xs_offset(xr0 + 32 * i, xc)]) = xreg[i];
+      *reinterpret_cast<u32x4*>(&xs[buf][xs_offset(xr0 + (kT / 8) * i, xc)]) = xreg[i];
   };
   auto load_w = [&](u32x4 (&wr)[NB][2], int kt) {
 #pragma unroll
@@ -363,14 +371,14 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   }
 }
 
-template <int BM, int BN, int MINB>
-__global__ __launch_bounds__(kThreads, MINB)
+template <int BM, int BN, int MINB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, MINB)
 void gemm_tiled_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                        const float* __restrict__ s, uint16_t* __restrict__ y,
                        float* __restrict__ part, int M, int N, int K, int gk,
                        int tiles_m, int tiles_n, int kt_per_split) {
-  tiled_body<BM, BN, false>(x, q, s, y, part, M, N, K, gk, tiles_m, tiles_n, kt_per_split,
-                            nullptr, nullptr);
+  tiled_body<BM, BN, false, WAVES>(x, q, s, y, part, M, N, K, gk, tiles_m, tiles_n, kt_per_split,
+                                   nullptr, nullptr);
 }
 
 template <int BM, int BN, int MINB>
@@ -379,8 +387,8 @@ void gemm_gated_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
                        const float* __restrict__ sg, const uint8_t* __restrict__ qu,
                        const float* __restrict__ su, uint16_t* __restrict__ h, int M, int N,
                        int K, int gk, int tiles_m, int tiles_n) {
-  tiled_body<BM, BN, true>(x, qg, sg, h, nullptr, M, N, K, gk, tiles_m, tiles_n,
-                           (K + kBK - 1) / kBK, qu, su);
+  tiled_body<BM, BN, true, 4>(x, qg, sg, h, nullptr, M, N, K, gk, tiles_m, tiles_n,
+                              (K + kBK - 1) / kBK, qu, su);
 }
 
 struct TiledPlan {
@@ -390,8 +398,9 @@ struct TiledPlan {
 
 // Tile and split choice from a cost model fitted to measurements on MI355X.
 // Work is counted in 128x128x64 MFMA steps; a CU runs its workgroups two
-// (128x256, 256x128: 240+ VGPRs) or three (128x128) at a time, and its
-// throughput depends on how many it holds (steps per microsecond, below).
+// (128x256 of 8 waves, 256x128 of 4 waves with 240+ VGPRs) or three
+// (128x128) at a time, and its throughput depends on how many it holds
+// (steps per microsecond, below).
 // The busiest CU sets the time: ceil(W / 256) workgroups of W, each taking
 // ceil(nkt / splits) steps. K splits add the fp32 partials' round trip
 // (4 bytes per output and split written and read back, 2 bytes of bf16
@@ -401,6 +410,7 @@ struct TiledPlan {
 // text-encoder shapes with few tiles split K.
 double cu_rate(int cfg, int64_t per_cu) {
   if (cfg == 2) return per_cu <= 1 ? 0.91 : per_cu == 2 ? 1.56 : 1.70;
+  if (cfg == 0) return per_cu <= 1 ? 1.69 : 1.90;
   return per_cu <= 1 ? 1.44 : 1.90;
 }
 
@@ -456,15 +466,15 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
   }
   const dim3 grid((uint32_t)(tiles_m * tiles_n), (uint32_t)p.splits);
   if (p.cfg == 0)
-    hipLaunchKernelGGL((gemm_tiled_kernel<128, 256, 2>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_tiled_kernel<128, 256, 2, 8>), grid, dim3(512), 0, stream,
                        x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
                        p.kt_per_split);
   else if (p.cfg == 1)
-    hipLaunchKernelGGL((gemm_tiled_kernel<256, 128, 2>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_tiled_kernel<256, 128, 2, 4>), grid, dim3(kThreads), 0, stream,
                        x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
                        p.kt_per_split);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<128, 128, 2>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_tiled_kernel<128, 128, 2, 4>), grid, dim3(kThreads), 0, stream,
                        x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
                        p.kt_per_split);
   hipError_t e = hipGetLastError();

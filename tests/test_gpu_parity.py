@@ -220,6 +220,21 @@ def test_linear_small_shapes(m, n, k, path):
     assert_bound(y, yr, ar, f"{path} {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (129, 2500, 4112), (1100, 2000, 2512), (1000, 4000, 2000), (1500, 4100, 784), (2047, 2500, 784),
+])
+def test_linear_wide_tile_shapes(m, n, k):
+    """Shapes the tile planner sends to the 128x256 tile (eight waves of one
+    32-column block each), with 8, 3, 2 and no K splits; M, N and K all end
+    in partial tiles or steps. Full compare against the oracle."""
+    x, w = random_problem(m + 5 * n + k, m, n, k)
+    q, s = O.quantize(w)
+    say("linear wide tile", m, n, k)
+    y = run_linear(x, q, s, F.PATH_AUTO)
+    yr, ar = O.linear_exact(x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"wide tile {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("path", ["tiled", "skinny"])
 def test_linear_tiny_workload(path):
     lin = generate("tiny").linears[0]
