@@ -23,8 +23,9 @@
 // runs step k's MFMAs from LDS and the decoded registers, then stages X for
 // step k+1 into the other LDS buffer. Two or three workgroups share each CU
 // (three with 128x128 tiles), so one workgroup's decode overlaps another's
-// MFMAs. The 128x256 tile runs 8 waves of one 32-column block each (about
-// 130 VGPRs, two workgroups per CU): per 128x128x64 step of work it moves
+// MFMAs. The 128x256 and 256x256 tiles run 8 waves of one 32-column block
+// each (128x256: about 130 VGPRs, two workgroups per CU; 256x256: about 200
+// VGPRs, one). For 128x256, per 128x128x64 step of work it moves
 // 16 KB of X and codes through the CU's vector-memory path against 24 KB
 // for two 128x128 workgroups, which measured 2-6% faster than both the
 // 4-wave 128x256 tile and 128x128 on the shapes that choose it (the load
@@ -392,39 +393,41 @@ void gemm_gated_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 }
 
 struct TiledPlan {
-  int cfg;          // 0: 128x256, 1: 256x128, 2: 128x128
+  int cfg;          // 0: 128x256, 1: 256x128, 2: 128x128, 3: 256x256
   int bm, bn, splits, kt_per_split;
 };
 
 // Tile and split choice from a cost model fitted to measurements on MI355X.
-// Work is counted in 128x128x64 MFMA steps; a CU runs its workgroups two
-// (128x256 of 8 waves, 256x128 of 4 waves with 240+ VGPRs) or three
-// (128x128) at a time, and its throughput depends on how many it holds
-// (steps per microsecond, below).
+// Work is counted in 128x128x64 MFMA steps; a CU runs its workgroups one
+// (256x256 of 8 waves, ~200 VGPRs), two (128x256 of 8 waves, 256x128 of 4
+// waves with 210+ VGPRs) or three (128x128) at a time, and its throughput
+// depends on how many it holds (steps per microsecond, below).
 // The busiest CU sets the time: ceil(W / 256) workgroups of W, each taking
 // ceil(nkt / splits) steps. K splits add the fp32 partials' round trip
 // (4 bytes per output and split written and read back, 2 bytes of bf16
-// out, at ~5 TB/s). Large square-ish shapes favour the 128x256 tile (more
-// reuse per load); shapes whose 128x128 tiles fill the CUs more evenly
-// (e.g. 2048x5120x5120, 1024x8192x8192, 3072^3) favour 128x128; 512-row
+// out, at ~5 TB/s). Large shapes favour the 256x256 tile (each step moves
+// 12 KB of X and codes per 128x128x64 of work through the CU, against 16 KB
+// for 128x256 and 24 KB for 128x128); shapes whose 128x128 tiles fill the
+// CUs more evenly (e.g. 2048x5120x5120, 3072^3) favour 128x128; 512-row
 // text-encoder shapes with few tiles split K.
 double cu_rate(int cfg, int64_t per_cu) {
   if (cfg == 2) return per_cu <= 1 ? 0.91 : per_cu == 2 ? 1.56 : 1.70;
   if (cfg == 0) return per_cu <= 1 ? 1.69 : 1.90;
+  if (cfg == 3) return 2.00;   // one workgroup per CU at a time
   return per_cu <= 1 ? 1.44 : 1.90;
 }
 
 TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
   const int nkt = (int)((k + kBK - 1) / kBK);
   // evaluation order breaks ties: 256x128 first below 2048 rows
-  const int order_small[3] = {1, 0, 2}, order_large[3] = {0, 1, 2};
+  const int order_small[4] = {1, 0, 2, 3}, order_large[4] = {3, 0, 1, 2};
   const int* order = m < 2048 ? order_small : order_large;
   TiledPlan best{2, 128, 128, 1, nkt};
   double best_cost = 1e30;
-  for (int oi = 0; oi < 3; ++oi) {
+  for (int oi = 0; oi < 4; ++oi) {
     const int cfg = order[oi];
-    const int bm = cfg == 1 ? 256 : 128, bn = cfg == 0 ? 256 : 128;
-    const int units = cfg == 2 ? 1 : 2;
+    const int bm = (cfg == 1 || cfg == 3) ? 256 : 128, bn = (cfg == 0 || cfg == 3) ? 256 : 128;
+    const int units = cfg == 2 ? 1 : cfg == 3 ? 4 : 2;
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
     for (int sp = 1; sp <= 8; ++sp) {
       const int steps = (nkt + sp - 1) / sp;
@@ -467,6 +470,10 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
   const dim3 grid((uint32_t)(tiles_m * tiles_n), (uint32_t)p.splits);
   if (p.cfg == 0)
     hipLaunchKernelGGL((gemm_tiled_kernel<128, 256, 2, 8>), grid, dim3(512), 0, stream,
+                       x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
+                       p.kt_per_split);
+  else if (p.cfg == 3)
+    hipLaunchKernelGGL((gemm_tiled_kernel<256, 256, 1, 8>), grid, dim3(512), 0, stream,
                        x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
                        p.kt_per_split);
   else if (p.cfg == 1)

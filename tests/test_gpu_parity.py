@@ -235,6 +235,21 @@ def test_linear_wide_tile_shapes(m, n, k):
     assert_bound(y, yr, ar, f"wide tile {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (3000, 1300, 2000), (2049, 2000, 2512), (700, 4100, 4112), (3000, 4100, 784), (2500, 5000, 784),
+])
+def test_linear_square_tile_shapes(m, n, k):
+    """Shapes the tile planner sends to the 256x256 tile (eight waves of one
+    32-column block each, 256 rows), with 3, 5 and no K splits; M, N and K
+    all end in partial tiles or steps. Full compare against the oracle."""
+    x, w = random_problem(m + 3 * n + 2 * k, m, n, k)
+    q, s = O.quantize(w)
+    say("linear square tile", m, n, k)
+    y = run_linear(x, q, s, F.PATH_AUTO)
+    yr, ar = O.linear_exact(x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"square tile {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("path", ["tiled", "skinny"])
 def test_linear_tiny_workload(path):
     lin = generate("tiny").linears[0]
