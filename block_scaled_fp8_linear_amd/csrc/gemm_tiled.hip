@@ -10,7 +10,7 @@
 //
 // Workgroup tile BM x BN, W waves side by side along N: wave w owns the
 // BN/W weight rows [n0 + w*BN/W, ...) for all BM rows of X (W = 4, or 8 for
-// the 128x256 tile, where each wave keeps one 32-column block). Every weight
+// the 128x256 and 256x256 tiles, where each wave keeps one 32-column block). Every weight
 // element is therefore decoded exactly once per workgroup (decode VALU per
 // MFMA flop falls as 1/BM), while the X tile is shared through LDS, staged
 // with 16-byte loads into an XOR-swizzled layout that the MFMA operand reads
@@ -489,8 +489,10 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
   return launch_reduce_partials(part, y, p.splits, m, n, stream);
 }
 
-// Gate/up pair: tiles as for a plain linear of the same shape, never split
-// (both accumulator sets live in registers to the end).
+// Gate/up pair: 128x128 tiles of four waves, two workgroups per CU, never
+// split (both accumulator sets live in registers to the end). An eight-wave
+// 128x256 gated tile measured slower: with one workgroup per CU its decode
+// no longer overlaps another workgroup's MFMAs.
 hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
                               const uint8_t* qu, const float* su, uint16_t* h,
                               int64_t m, int64_t n, int64_t k, hipStream_t stream) {
