@@ -6,9 +6,12 @@
 //   amax = max |w|;  S = fl32(amax / 448), or 1 when amax == 0;
 //   code = nearest finite E4M3 to fl32(w / S), ties to the even code,
 //          saturating at 448, sign kept.
-// One workgroup per block; offline work, so every element takes an IEEE
-// division. The input is fp32, or bf16 widened exactly to fp32 (a
-// checkpoint stored in bf16).
+// One workgroup of eight waves per block, each lane holding 32 elements in
+// registers between the amax and the encode; offline work, so every element
+// takes an IEEE division. The input is fp32, or bf16 widened exactly to fp32
+// (a checkpoint stored in bf16). Wave loads cover whole block rows: lanes
+// that each took one row's 64-column half (a wave load touching 64 separate
+// lines) measured 4-6x slower on MI355X.
 #include "fp8bl_device.h"
 #include "fp8bl_internal.h"
 
@@ -41,51 +44,53 @@ __device__ __forceinline__ f32x4 load4(const uint16_t* w, size_t i) {
                __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xFFFF0000u)};
 }
 
+constexpr int kQThreads = 512;
+
 template <typename T>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kQThreads)
 void quantize_kernel(const T* __restrict__ w, uint8_t* __restrict__ q,
                      float* __restrict__ s, int N, int K, int gk) {
-  __shared__ float wave_max[kThreads / 64];
+  __shared__ float wave_max[kQThreads / 64];
   const int bi = blockIdx.y, bj = blockIdx.x;
   const int tid = threadIdx.x;
-  // Thread t covers row (t >> 1) of the block, columns (t & 1) * 64 .. +64.
-  const int row = bi * kBlock + (tid >> 1);
-  const int col0 = bj * kBlock + (tid & 1) * 64;
-  const bool row_ok = row < N;
+  // Wave w covers block rows 16 w .. 16 w + 15; pass i of its lane l takes
+  // row 16 w + 2 i + (l >> 5), columns 4 (l & 31) .. +4, so each wave load
+  // reads two whole 128-column block rows (contiguous runs).
+  const int row0 = bi * kBlock + (tid >> 6) * 16 + ((tid >> 5) & 1);
+  const int col = bj * kBlock + (tid & 31) * 4;
+  // K % 16 == 0 and col % 4 == 0: a group of four is wholly inside or outside K
+  const bool col_ok = col < K;
 
-  f32x4 v[16];
+  f32x4 v[8];
   float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const int col = col0 + c * 4;
-    if (row_ok && col < K) {
-      v[c] = load4(w, (size_t)row * K + col);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])),
-                               fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
+  for (int i = 0; i < 8; ++i) {
+    const int row = row0 + 2 * i;
+    if (col_ok && row < N) {
+      v[i] = load4(w, (size_t)row * K + col);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])),
+                               fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
     } else {
-      v[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  amax = fmaxf(fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3])),
+               fmaxf(fmaxf(wave_max[4], wave_max[5]), fmaxf(wave_max[6], wave_max[7])));
   const float sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
   if (tid == 0) s[bi * gk + bj] = sc;
-  if (!row_ok) return;
+  if (!col_ok) return;
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const int col = col0 + c4 * 16;
-    if (col >= K) break;
-    u32x4 out;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f32x4 t = v[c4 * 4 + d];
-      out[d] = e4m3x2_hw<true>(__fdiv_rn(t[2], sc), __fdiv_rn(t[3], sc),
-                               e4m3x2_hw<false>(__fdiv_rn(t[0], sc), __fdiv_rn(t[1], sc), 0u));
-    }
-    *reinterpret_cast<u32x4*>(q + (size_t)row * K + col) = out;
+  for (int i = 0; i < 8; ++i) {
+    const int row = row0 + 2 * i;
+    if (row >= N) break;
+    const f32x4 t = v[i];
+    *reinterpret_cast<uint32_t*>(q + (size_t)row * K + col) =
+        e4m3x2_hw<true>(__fdiv_rn(t[2], sc), __fdiv_rn(t[3], sc),
+                        e4m3x2_hw<false>(__fdiv_rn(t[0], sc), __fdiv_rn(t[1], sc), 0u));
   }
 }
 
@@ -165,7 +170,7 @@ hipError_t launch_quantize(const float* w, uint8_t* q, float* s, int64_t n, int6
                            hipStream_t stream) {
   const int gn = (int)((n + kBlock - 1) / kBlock);
   const int gk = (int)((k + kBlock - 1) / kBlock);
-  hipLaunchKernelGGL(quantize_kernel<float>, dim3((uint32_t)gk, (uint32_t)gn), dim3(kThreads), 0,
+  hipLaunchKernelGGL(quantize_kernel<float>, dim3((uint32_t)gk, (uint32_t)gn), dim3(kQThreads), 0,
                      stream, w, q, s, (int)n, (int)k, gk);
   return hipGetLastError();
 }
@@ -174,7 +179,7 @@ hipError_t launch_quantize_bf16(const uint16_t* w, uint8_t* q, float* s, int64_t
                                 hipStream_t stream) {
   const int gn = (int)((n + kBlock - 1) / kBlock);
   const int gk = (int)((k + kBlock - 1) / kBlock);
-  hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((uint32_t)gk, (uint32_t)gn), dim3(kThreads), 0,
+  hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((uint32_t)gk, (uint32_t)gn), dim3(kQThreads), 0,
                      stream, w, q, s, (int)n, (int)k, gk);
   return hipGetLastError();
 }
