@@ -117,7 +117,7 @@ __device__ __forceinline__ void schedule_operand_reads() {
 // GATED: the MLP gate/up pair in one pass. The same X tile feeds two weights
 // (q, s = gate; q2, s2 = up) into two accumulator sets and the epilogue
 // writes swiglu(gate, up) instead of either product.
-template <int BM, int BN, bool GATED, int WAVES>
+template <int BM, int BN, bool GATED, int WAVES, bool PAIRED = false>
 __device__ __forceinline__
 void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                 const float* __restrict__ s, uint16_t* __restrict__ y,
@@ -131,6 +131,11 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   constexpr int XCH = BM * kBK / 8 / kT;  // 16-byte X chunks per thread per step
   static_assert(WN % 32 == 0 && 128 % WN == 0, "wave rows must sit in one scale block");
   static_assert(XCH >= 1, "tile too small");
+  // PAIRED: the first WAVES/2 waves run weight (q, s) and the others weight
+  // (q2, s2), over the same BN/2 output columns of the tile.
+  constexpr int BNO = PAIRED ? BN / 2 : BN;   // output columns per tile
+  static_assert(!(PAIRED && GATED), "one pairing mode at a time");
+  static_assert(!PAIRED || 2 * kBK >= BNO, "the exchange tile must fit the X buffers");
 
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kBK];
 
@@ -153,7 +158,7 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   const int tm = first_m + in_group % gsize;
   const int tn = in_group / gsize;
   const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  const int n0 = tn * BNO;
 
   const int nkt = (K + kBK - 1) / kBK;
   const int kt0 = blockIdx.y * kt_per_split;
@@ -169,15 +174,19 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
 
   // ---- W codes: lane holds 16 codes of row (lane % 32) of each column
   // block, k chunk (lane / 32) of each 32-wide k slab.
+  const bool upper = PAIRED && wave >= WAVES / 2;
+  const int wslot = upper ? wave - WAVES / 2 : wave;   // column slot of the wave's rows
+  const uint8_t* __restrict__ qw = upper ? q2 : q;
+  const float* __restrict__ sw = upper ? s2 : s;
   const __amdgpu_buffer_rsrc_t wrs =
-      make_rsrc(q + (size_t)n0 * K, (uint32_t)(max(min(N - n0, BN), 0) * K));
+      make_rsrc(qw + (size_t)n0 * K, (uint32_t)(max(min(N - n0, BNO), 0) * K));
   const __amdgpu_buffer_rsrc_t wrs2 =
       make_rsrc((GATED ? q2 : q) + (size_t)n0 * K, (uint32_t)(max(min(N - n0, BN), 0) * K));
   const int wkoff = (lane >> 5) * 16;
-  const uint32_t woff0 = (uint32_t)((wave * WN + (lane & 31)) * K + wkoff);
+  const uint32_t woff0 = (uint32_t)((wslot * WN + (lane & 31)) * K + wkoff);
   const uint32_t wnb_stride = (uint32_t)(32 * K);
-  const int srow = (n0 + wave * WN) / kBlock;
-  const bool wave_live = (n0 + wave * WN) < N;
+  const int srow = (n0 + wslot * WN) / kBlock;
+  const bool wave_live = (n0 + wslot * WN) < N;
 
   u32x4 xreg[XCH];
   auto load_x = [&](int kt) {
@@ -205,7 +214,7 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   auto scale_of = [&](int kt) -> float {
     // always a valid address (clamped block column), zero for dead waves
     const int kb = min((kt * kBK) / kBlock, gk - 1);
-    const float v = s[(wave_live ? srow : 0) * gk + kb];
+    const float v = sw[(wave_live ? srow : 0) * gk + kb];
     return wave_live ? v : 0.0f;
   };
   // The same two for the second (up) weight of a gated tile.
@@ -331,8 +340,46 @@ void tiled_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
 
   // ---- Epilogue. acc[mb][nb][r] holds row mb*32 + (r/4)*8 + (l/32)*4 + r%4,
   // column nb*32 + l%32 of the wave's sub-tile.
-  const int col_base = n0 + wave * WN + (lane & 31);
+  const int col_base = n0 + wslot * WN + (lane & 31);
   const int row_base = m0 + (lane >> 5) * 4;
+  if constexpr (PAIRED) {
+    // The upper waves hand their products, rounded to bf16 (the rounding the
+    // SwiGLU applies to them first anyway), to the lower waves through the X
+    // buffers: a BM x BNO bf16 tile.
+    uint16_t* ex = &xs[0][0];
+    const int exc = wslot * WN + (lane & 31);
+    __syncthreads();
+    if (upper) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = mb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            ex[rl * BNO + exc + nb * 32] = __builtin_bit_cast(uint16_t, (__bf16)acc[mb][nb][r]);
+          }
+    }
+    __syncthreads();
+    if (!upper) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = col_base + nb * 32;
+          if (col >= N) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = mb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            if (m0 + rl < M) {
+              const float u = __builtin_bit_cast(float, (uint32_t)ex[rl * BNO + exc + nb * 32] << 16);
+              y[(size_t)(m0 + rl) * N + col] = swiglu_bf16(acc[mb][nb][r], u);
+            }
+          }
+        }
+    }
+    return;
+  }
   if (gridDim.y == 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -390,6 +437,16 @@ void gemm_gated_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
                        int K, int gk, int tiles_m, int tiles_n) {
   tiled_body<BM, BN, true, 4>(x, qg, sg, h, nullptr, M, N, K, gk, tiles_m, tiles_n,
                               (K + kBK - 1) / kBK, qu, su);
+}
+
+template <int BM, int BN, int MINB>
+__global__ __launch_bounds__(512, MINB)
+void gemm_gated_paired_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qg,
+                              const float* __restrict__ sg, const uint8_t* __restrict__ qu,
+                              const float* __restrict__ su, uint16_t* __restrict__ h, int M, int N,
+                              int K, int gk, int tiles_m, int tiles_n) {
+  tiled_body<BM, BN, false, 8, true>(x, qg, sg, h, nullptr, M, N, K, gk, tiles_m, tiles_n,
+                                     (K + kBK - 1) / kBK, qu, su);
 }
 
 struct TiledPlan {
@@ -489,19 +546,46 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
   return launch_reduce_partials(part, y, p.splits, m, n, stream);
 }
 
-// Gate/up pair: 128x128 tiles of four waves, two workgroups per CU, never
-// split (both accumulator sets live in registers to the end). An eight-wave
-// 128x256 gated tile measured slower: with one workgroup per CU its decode
-// no longer overlaps another workgroup's MFMAs.
+// Gate/up pair, never split (the SwiGLU needs whole sums). Two kernels:
+//  - from 2048 rows, 128x128 tiles of four waves that each run both weights
+//    (two accumulator sets fed by one X fragment read), two workgroups per
+//    CU: X is staged once for both weights;
+//  - below that, a paired tile of eight waves, the first four running gate
+//    rows and the other four the matching up rows of the same 128 output
+//    columns, one accumulator set per wave; the up half hands its bf16
+//    products to the gate half through LDS for the SwiGLU. Its 256-row
+//    (one workgroup per CU) or 128-row (two) form is picked by the tiled
+//    planner's kind of cost model, with per-CU rates fitted to measurements
+//    on MI355X (steps of 128x128x64 per microsecond).
+// Same-box A/B (bit-identical outputs): the paired tile is 5% faster on
+// 512x25600x5120 and up to 11% on shapes of a few hundred rows; the
+// two-weight tile is 4-5% faster from 2048 rows. An eight-wave 128x256
+// tile with both weights in every wave measured slower than both.
 hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
                               const uint8_t* qu, const float* su, uint16_t* h,
                               int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const int gk = (int)((k + kBlock - 1) / kBlock);
-  const int tiles_m = (int)((m + 127) / 128);
   const int tiles_n = (int)((n + 127) / 128);
-  hipLaunchKernelGGL((gemm_gated_kernel<128, 128, 2>), dim3((uint32_t)(tiles_m * tiles_n), 1),
-                     dim3(kThreads), 0, stream, x, qg, sg, qu, su, h, (int)m, (int)n, (int)k, gk,
-                     tiles_m, tiles_n);
+  if (m >= 2048) {
+    const int tiles_m = (int)((m + 127) / 128);
+    hipLaunchKernelGGL((gemm_gated_kernel<128, 128, 2>), dim3((uint32_t)(tiles_m * tiles_n), 1),
+                       dim3(kThreads), 0, stream, x, qg, sg, qu, su, h, (int)m, (int)n, (int)k,
+                       gk, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
+  const int tm256 = (int)((m + 255) / 256), tm128 = (int)((m + 127) / 128);
+  const int64_t per_cu256 = ((int64_t)tm256 * tiles_n + 255) / 256;
+  const int64_t per_cu128 = ((int64_t)tm128 * tiles_n + 255) / 256;
+  const double cost256 = (double)per_cu256 * 4 / 2.2;
+  const double cost128 = (double)per_cu128 * 2 / (per_cu128 <= 1 ? 1.51 : 2.09);
+  if (cost256 < cost128)
+    hipLaunchKernelGGL((gemm_gated_paired_kernel<256, 256, 1>),
+                       dim3((uint32_t)(tm256 * tiles_n), 1), dim3(512), 0, stream, x, qg, sg, qu,
+                       su, h, (int)m, (int)n, (int)k, gk, tm256, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_gated_paired_kernel<128, 256, 2>),
+                       dim3((uint32_t)(tm128 * tiles_n), 1), dim3(512), 0, stream, x, qg, sg, qu,
+                       su, h, (int)m, (int)n, (int)k, gk, tm128, tiles_n);
   return hipGetLastError();
 }
 

@@ -57,9 +57,24 @@ def test_mlp_small_shapes(m, n, k):
     _check_full(x, qg, sg, qu, su, h, f"mlp {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (1000, 5000, 272),    # below 2048 rows, many tiles: the 256-row paired tile
+    (2100, 300, 528),     # from 2048 rows: the tile with both weights in every wave
+])
+def test_mlp_larger_shapes_each_kernel(m, n, k):
+    """Ragged shapes (partial row and column tiles, K not a multiple of 64)
+    that the gate/up planner sends to the kernels the small shapes above do
+    not reach, compared in full."""
+    x, qg, sg, qu, su = _pair(m + 3 * n + k, m, n, k)
+    say("mlp gate/up", m, n, k)
+    h = run_mlp(x, qg, sg, qu, su)
+    _check_full(x, qg, sg, qu, su, h, f"mlp {m}x{n}x{k}")
+
+
 def test_mlp_matches_separate_linears():
-    """At a shape where the plain linear runs the same 128x128 tiles without
-    split-K, its g and u are the fused kernel's g and u bit for bit, so the
+    """At a shape where the plain linear does not split K, its g and u are the
+    fused kernel's g and u bit for bit (every tile shape accumulates an output
+    in the same order), so the
     fused h must be the SwiGLU of the two plain outputs up to silu's fp32
     evaluation: equal almost everywhere, never more than one bf16 ulp off."""
     m, n, k = 1024, 4096, 1024
