@@ -558,8 +558,9 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
 //    planner's kind of cost model, with per-CU rates fitted to measurements
 //    on MI355X (steps of 128x128x64 per microsecond).
 // Same-box A/B (bit-identical outputs): the paired tile is 5% faster on
-// 512x25600x5120 and up to 11% on shapes of a few hundred rows; the
-// two-weight tile is 4-5% faster from 2048 rows. An eight-wave 128x256
+// 512x25600x5120, up to 11% on shapes of a few hundred rows and 1-4% at
+// 1024-1536 rows (one shape within 1% the other way); the two-weight tile
+// is 2-6% faster from 2048 rows. An eight-wave 128x256
 // tile with both weights in every wave measured slower than both.
 hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
                               const uint8_t* qu, const float* su, uint16_t* h,
