@@ -328,7 +328,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer would shard by rows of X, columns or rows of W; see DESIGN.md).",
+              "(the layer would shard by rows of X, or by columns or rows of W with a "
+              "gather or sum of the partial outputs across GPUs).",
               file=sys.stderr)
         sys.exit(2)
 
