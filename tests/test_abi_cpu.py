@@ -159,8 +159,8 @@ def test_linear_workspace_errors(lib):
 
 def test_valid_call_without_gpu_reports_device_status(lib):
     """With valid arguments the gate runs; on a machine without a gfx950 it
-    must answer with a status, not crash. (On the GPU machine this test is not
-    meaningful and is skipped.)"""
+    must answer with a status, not crash. (With a GPU present this test is
+    not meaningful and is skipped.)"""
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
