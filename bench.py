@@ -45,12 +45,18 @@ WORKLOADS = {
     "tiny": ("tiny", 0, "mfma"),
 }
 
+# The HBM-bound half of the metric, measured after the headline line.
+SECONDARY = ("skinny_m16", "skinny_m1")
+
+# --path values -> fp8bl_path
+PATHS = {"auto": 0, "tiled": 1, "skinny": 2, "large": 3}
+
 
 # What one timed launch (one library call per step) runs on the GPU; the
 # rocprofv3 summaries list these kernels with their own averages, which add
 # up to avg_launch_us.
 LAUNCH_KERNELS = {
-    "linear": "fp8_block_linear: gemm_tiled_kernel or gemm_skinny_kernel, "
+    "linear": "fp8_block_linear: gemm_large_kernel, gemm_tiled_kernel or gemm_skinny_kernel, "
               "+ reduce_partials_kernel when K is split",
     "dequant": "fp8_block_dequant: dequant_kernel",
     "quantize": "fp8_block_quantize: quantize_kernel<float>",
@@ -68,6 +74,7 @@ KERNEL_SOURCES = {
     "gemm_tiled_kernel": ("gemm_tiled.hip",),
     "gemm_gated_kernel": ("gemm_tiled.hip",),
     "gemm_gated_paired_kernel": ("gemm_tiled.hip",),
+    "gemm_large_kernel": ("gemm_large.hip",),
     "gemm_skinny_kernel": ("gemm_skinny.hip",),
     "reduce_partials_kernel": ("gemm_skinny.hip",),
     "dequant_kernel": ("dequant.hip",),
@@ -289,13 +296,178 @@ def stream_ceiling(nbytes=1 << 30, reps=10):
     return out
 
 
+def measure(args, workload, op="linear", path="auto", steps=None, warmup=None):
+    """Time `steps` launches of one library call on `workload` (inputs resident
+    in HBM, rotated over enough buffer sets to defeat the MALL) and return the
+    throughput and roofline fields of one result."""
+    import torch
+
+    import block_scaled_fp8_linear_amd as F
+    from workloads import generate
+
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    gen_name, idx, bound = WORKLOADS[workload]
+    wl = generate(gen_name)
+    lin = wl.linears[idx]
+    m, n, k = lin.m, lin.n, lin.k
+    x_bits = lin.x
+    if x_bits is None:                   # the MLP down input: any bf16 of that shape
+        from workloads import draw_x
+        x_bits = draw_x(np.random.default_rng(wl.seed + 100), m, k)
+
+    dev = torch.device("cuda:0")
+    if not F.device_supported(0):
+        raise RuntimeError("cuda:0 is not a gfx950 device")
+    set_bytes = 2 * m * k + n * k + 2 * m * n
+    if op == "mlp":
+        set_bytes += n * k
+    rotate = args.rotate or int(min(64, max(1, -(-2 * MALL_BYTES // set_bytes))))
+
+    w_dev = torch.from_numpy(lin.w).to(dev)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    sets = []
+    for r in range(rotate):
+        q, s = F.fp8_block_quantize(w_dev)
+        x = x0.clone()
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        sets.append((x, q, s, y))
+    del w_dev
+    if op == "mlp":
+        # the up weight of the pair, one copy per set like the gate weight
+        wu_dev = torch.from_numpy(wl.linears[idx + 1].w).to(dev)
+        ups = [F.fp8_block_quantize(wu_dev) for _ in range(rotate)]
+        del wu_dev
+    ws_bytes = F.workspace_size(m, n, k)
+    if op in ("w8a8", "w8a8_gemm"):
+        ws_bytes = F.w8a8_workspace_size(m, n, k)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    if op == "dequant":
+        wouts = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
+    if op == "w8a8_gemm":
+        xqs = [F.fp8_act_quantize(st[0]) for st in sets]
+    if op == "quantize":
+        w_srcs = [torch.from_numpy(lin.w).to(dev) for _ in range(min(rotate, 4))]
+    path_id = PATHS[path]
+
+    def step(i):
+        x, q, s, y = sets[i % rotate]
+        if op == "linear":
+            F.fp8_block_linear(x, q, s, out=y, workspace=ws, path=path_id)
+        elif op == "w8a8":
+            F.fp8_block_linear_w8a8_bf16(x, q, s, out=y, workspace=ws)
+        elif op == "w8a8_gemm":
+            xq, xs = xqs[i % rotate]
+            F.fp8_block_linear_w8a8(xq, xs, q, s, out=y, workspace=ws)
+        elif op == "mlp":
+            qu, su = ups[i % rotate]
+            F.fp8_block_mlp_gate_up(x, q, s, qu, su, out=y)
+        elif op == "dequant":
+            F.fp8_block_dequant(q, s, out=wouts[i % rotate])
+        else:
+            F.fp8_block_quantize(w_srcs[i % len(w_srcs)], q, s)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        # The K steps are captured once into a HIP graph and replayed, so the
+        # host-side cost of K separate calls stays off the timed path.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                step(i)
+        graph.replay()                    # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    gpu_s = e0.elapsed_time(e1) / 1e3
+    # per-launch average over the timed region, from HIP events on the launch
+    # stream (a launch = one library call; with split-K that is the GEMM
+    # kernel plus the ordered reduce kernel)
+    avg_launch_s = gpu_s / steps
+
+    flops = 2.0 * m * n * k
+    abytes = alg_bytes(m, n, k)
+    gn, gk = -(-n // 128), -(-k // 128)
+    if op == "dequant":          # 1 B code in, 2 B bf16 out, plus the scale grid
+        bound, flops, abytes = "hbm", 0.0, 3 * n * k + 4 * gn * gk
+    elif op == "quantize":       # 4 B fp32 in, 1 B code out, plus the scale grid
+        bound, flops, abytes = "hbm", 0.0, 5 * n * k + 4 * gn * gk
+    elif op == "mlp":            # two products over one X, one bf16 output
+        flops = 4.0 * m * n * k
+        abytes = 2 * m * k + 2 * (n * k + 4 * gn * gk) + 2 * m * n
+    mfma_peak, dtype = MFMA_BF16_PEAK_TFLOPS, "bf16"
+    if op in ("w8a8", "w8a8_gemm"):
+        # E4M3 x E4M3 products on the fp8 matrix cores, fp32 accumulation
+        mfma_peak, dtype = MFMA_FP8_PEAK_TFLOPS, "fp8_e4m3"
+        abytes = (m * k + 4 * m * -(-k // 128) + n * k + 4 * gn * gk + 2 * m * n
+                  + (3 * m * k if op == "w8a8" else 0))
+    if bound == "hbm":
+        unit, value = "GB/s", abytes * steps / wall / 1e9
+        achieved, peak, r_unit = abytes / avg_launch_s / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        unit, value = "TFLOP/s", flops * steps / wall / 1e12
+        achieved, peak, r_unit = flops / avg_launch_s / 1e12, mfma_peak, "TFLOP/s"
+    traffic_key = workload if op == "linear" else f"{op}:{workload}"
+    if path != "auto":
+        traffic_key += f"@{path}"
+    roof = {
+        "bound": bound,
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": r_unit,
+        "frac": round(achieved / peak, 4),
+        "traffic": measured_traffic(traffic_key),
+        "avg_launch_us": round(avg_launch_s * 1e6, 3),
+        "launch": LAUNCH_KERNELS[op],
+        "alg_bytes": abytes,
+        "flops": flops,
+    }
+    if op == "linear" and bound == "hbm":
+        # the weight stream alone (codes + scale grid), the part that scales with N*K
+        wbytes = n * k + 4 * gn * gk
+        roof["weight_GBps"] = round(wbytes / avg_launch_s / 1e9, 1)
+    del sets, ws
+    torch.cuda.empty_cache()
+    return {
+        "value": value, "unit": unit, "wall": wall, "dtype": dtype, "roofline": roof,
+        "m": m, "n": n, "k": k, "rotate": rotate, "lin": lin, "x_bits": x_bits, "bound": bound,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dit_mlp_up", choices=sorted(WORKLOADS),
+                    help="the workload of the headline line (default: the M=16384 DiT MLP "
+                         "up projection, 16384x12288x3072)")
+    ap.add_argument("--path", default="auto", choices=sorted(PATHS),
+                    help="kernel choice for --op linear (auto: the library's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the skinny-M (M=16, M=1) HBM-bound lines")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0 = auto)")
     ap.add_argument("--op", default="linear",
                     choices=["linear", "dequant", "quantize", "mlp", "w8a8", "w8a8_gemm"],
@@ -333,173 +505,47 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
-    import block_scaled_fp8_linear_amd as F
-    from workloads import generate
-
     if args.op == "mlp" and args.workload != "mlp_gate":
         print("--op mlp runs on the gate/up pair: use --workload mlp_gate", file=sys.stderr)
         sys.exit(2)
-    gen_name, idx, bound = WORKLOADS[args.workload]
-    wl = generate(gen_name)
-    lin = wl.linears[idx]
-    m, n, k = lin.m, lin.n, lin.k
-    x_bits = lin.x
-    if x_bits is None:                   # the MLP down input: any bf16 of that shape
-        from workloads import draw_x
-        x_bits = draw_x(np.random.default_rng(wl.seed + 100), m, k)
 
-    dev = torch.device("cuda:0")
-    if not F.device_supported(0):
-        raise RuntimeError("cuda:0 is not a gfx950 device")
-    set_bytes = 2 * m * k + n * k + 2 * m * n
-    if args.op == "mlp":
-        set_bytes += n * k
-    rotate = args.rotate or int(min(64, max(1, -(-2 * MALL_BYTES // set_bytes))))
-
-    w_dev = torch.from_numpy(lin.w).to(dev)
-    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    sets = []
-    for r in range(rotate):
-        q, s = F.fp8_block_quantize(w_dev)
-        x = x0.clone()
-        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        sets.append((x, q, s, y))
-    del w_dev
-    if args.op == "mlp":
-        # the up weight of the pair, one copy per set like the gate weight
-        wu_dev = torch.from_numpy(wl.linears[idx + 1].w).to(dev)
-        ups = [F.fp8_block_quantize(wu_dev) for _ in range(rotate)]
-        del wu_dev
-    ws_bytes = F.workspace_size(m, n, k)
-    if args.op in ("w8a8", "w8a8_gemm"):
-        ws_bytes = F.w8a8_workspace_size(m, n, k)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    if args.op == "dequant":
-        wouts = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
-    if args.op == "w8a8_gemm":
-        xqs = [F.fp8_act_quantize(st[0]) for st in sets]
-    if args.op == "quantize":
-        w_srcs = [torch.from_numpy(lin.w).to(dev) for _ in range(min(rotate, 4))]
-
-    def step(i):
-        x, q, s, y = sets[i % rotate]
-        if args.op == "linear":
-            F.fp8_block_linear(x, q, s, out=y, workspace=ws)
-        elif args.op == "w8a8":
-            F.fp8_block_linear_w8a8_bf16(x, q, s, out=y, workspace=ws)
-        elif args.op == "w8a8_gemm":
-            xq, xs = xqs[i % rotate]
-            F.fp8_block_linear_w8a8(xq, xs, q, s, out=y, workspace=ws)
-        elif args.op == "mlp":
-            qu, su = ups[i % rotate]
-            F.fp8_block_mlp_gate_up(x, q, s, qu, su, out=y)
-        elif args.op == "dequant":
-            F.fp8_block_dequant(q, s, out=wouts[i % rotate])
-        else:
-            F.fp8_block_quantize(w_srcs[i % len(w_srcs)], q, s)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    if args.eager:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(args.steps):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        # The K steps are captured once into a HIP graph and replayed, so the
-        # host-side cost of K separate calls stays off the timed path.
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        graph.replay()                    # untimed: first replay uploads the graph
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    gpu_s = e0.elapsed_time(e1) / 1e3
-    # per-launch average over the timed region, from HIP events on the launch
-    # stream (a launch = one fp8_block_linear call; with split-K that is the
-    # GEMM kernel plus the ordered reduce kernel)
-    avg_launch_s = gpu_s / args.steps
-
-    flops = 2.0 * m * n * k
-    abytes = alg_bytes(m, n, k)
-    gn, gk = -(-n // 128), -(-k // 128)
-    if args.op == "dequant":          # 1 B code in, 2 B bf16 out, plus the scale grid
-        bound, flops, abytes = "hbm", 0.0, 3 * n * k + 4 * gn * gk
-    elif args.op == "quantize":       # 4 B fp32 in, 1 B code out, plus the scale grid
-        bound, flops, abytes = "hbm", 0.0, 5 * n * k + 4 * gn * gk
-    elif args.op == "mlp":            # two products over one X, one bf16 output
-        flops = 4.0 * m * n * k
-        abytes = 2 * m * k + 2 * (n * k + 4 * gn * gk) + 2 * m * n
-    mfma_peak, dtype = MFMA_BF16_PEAK_TFLOPS, "bf16"
-    if args.op in ("w8a8", "w8a8_gemm"):
-        # E4M3 x E4M3 products on the fp8 matrix cores, fp32 accumulation
-        mfma_peak, dtype = MFMA_FP8_PEAK_TFLOPS, "fp8_e4m3"
-        abytes = (m * k + 4 * m * -(-k // 128) + n * k + 4 * gn * gk + 2 * m * n
-                  + (3 * m * k if args.op == "w8a8" else 0))
-    if bound == "hbm":
-        unit, value = "GB/s", abytes * args.steps / wall / 1e9
-        achieved, peak, r_unit = abytes / avg_launch_s / 1e9, HBM_PEAK_GBPS, "GB/s"
-    else:
-        unit, value = "TFLOP/s", flops * args.steps / wall / 1e12
-        achieved, peak, r_unit = flops / avg_launch_s / 1e12, mfma_peak, "TFLOP/s"
-
+    r = measure(args, args.workload, args.op, args.path)
+    m, n, k = r["m"], r["n"], r["k"]
     out = {
         "metric": "FP8-block linear TFLOP/s (% bf16 MFMA peak) and weight GB/s (% HBM) at M<=32",
-        "value": round(value, 3),
-        "unit": unit,
+        "value": round(r["value"], 3),
+        "unit": r["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "ms_per_step": round(r["wall"] / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": r["dtype"],
         "data": "synthetic",
-        "config": {"workload": args.workload, "op": args.op, "m": m, "n": n, "k": k,
-                   "weight": "e4m3 + fp32 128x128 scale_inv", "rotated_sets": rotate,
+        "config": {"workload": args.workload, "op": args.op, "path": args.path, "m": m, "n": n,
+                   "k": k, "weight": "e4m3 + fp32 128x128 scale_inv",
+                   "rotated_sets": r["rotate"],
                    "launch": "eager" if args.eager else "hip graph of K steps",
                    "parallelism": "none (1 GPU)"},
-        "roofline": {
-            "bound": bound,
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": r_unit,
-            "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(args.workload if args.op == "linear" else f"{args.op}:{args.workload}"),
-            "avg_launch_us": round(avg_launch_s * 1e6, 3),
-            "launch": LAUNCH_KERNELS[args.op],
-            "alg_bytes": abytes,
-            "flops": flops,
-        },
+        "roofline": r["roofline"],
     }
-    if args.op == "linear" and bound == "hbm":
-        # the weight stream alone (codes + scale grid), the part that scales with N*K
-        wbytes = n * k + 4 * gn * gk
-        out["roofline"]["weight_GBps"] = round(wbytes / avg_launch_s / 1e9, 1)
+    if args.op == "linear" and not args.no_secondary and args.workload not in SECONDARY:
+        # The metric's other half: the HBM-bound skinny shapes (M <= 32), each
+        # timed the same way (its own rotated buffer sets, graph replay).
+        sec = []
+        for wname in SECONDARY:
+            rs = measure(args, wname, "linear", "auto", steps=max(args.steps, 200),
+                         warmup=args.warmup)
+            sec.append({"workload": wname, "m": rs["m"], "n": rs["n"], "k": rs["k"],
+                        "value": round(rs["value"], 3), "unit": rs["unit"],
+                        "rotated_sets": rs["rotate"], "roofline": rs["roofline"]})
+        out["secondary"] = sec
     if not args.no_cpu_baseline and args.op == "linear":
-        cb = cpu_baseline(lin, x_bits)
+        cb = cpu_baseline(r["lin"], r["x_bits"])
         rows, passes = cb.pop("rows"), cb.pop("passes")
-        if bound == "hbm":
+        if r["bound"] == "hbm":
             # oracle throughput expressed in the metric's unit (bytes of the sample)
             cb["value"] = alg_bytes(rows, n, k) * passes / cb.pop("seconds") / 1e9
             cb["unit"] = "GB/s"

@@ -25,6 +25,7 @@ FP8BL_HIP_ERROR = 5
 PATH_AUTO = 0
 PATH_TILED = 1
 PATH_SKINNY = 2
+PATH_LARGE = 3
 
 _lib = None
 

@@ -20,6 +20,9 @@ constexpr int64_t kMaxElems = (int64_t)1 << 35;   // N*K, M*K and M*N stay below
 constexpr int kSkinnyMaxM = 32;
 // The GEMM kernels address a tile's rows with 32-bit buffer offsets.
 constexpr int64_t kMaxLinearK = (int64_t)1 << 20;
+// The large-tile kernel also stores 256 output rows (fp32 partials) through
+// one buffer descriptor: 256 * N * 4 bytes must stay below 2^31.
+constexpr int64_t kLargeMaxN = (int64_t)1 << 21;
 
 // 0 = unknown, 1 = gfx950, 2 = other.
 std::atomic<int> g_arch[kMaxDevices];
@@ -61,8 +64,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP8BL_OK : FP8BL_HIP_ERR
 
 int validate_linear(const uint16_t* x, const uint8_t* q, const float* s, const uint16_t* y,
                     int64_t m, int64_t n, int64_t k, int path) {
-  if (path != FP8BL_PATH_AUTO && path != FP8BL_PATH_TILED && path != FP8BL_PATH_SKINNY)
+  if (path != FP8BL_PATH_AUTO && path != FP8BL_PATH_TILED && path != FP8BL_PATH_SKINNY &&
+      path != FP8BL_PATH_LARGE)
     return FP8BL_INVALID_ARG;
+  if (path == FP8BL_PATH_LARGE && n >= kLargeMaxN) return FP8BL_INVALID_ARG;
   if (m < 0 || m >= kMaxDim) return FP8BL_INVALID_ARG;
   int st = check_nk(n, k);
   if (st != FP8BL_OK) return st;
@@ -155,8 +160,12 @@ FP8BL_EXPORT int fp8_block_dequant(const uint8_t* q, const float* scale_inv, uin
 FP8BL_EXPORT size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || (k % 16) != 0) return 0;
   if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return 0;
-  const size_t a = fp8bl::tiled_workspace_bytes(m, n, k);
+  size_t a = fp8bl::tiled_workspace_bytes(m, n, k);
   const size_t b = fp8bl::skinny_workspace_bytes(m, n, k);
+  if (n < kLargeMaxN) {
+    const size_t c = fp8bl::large_workspace_bytes(m, n, k);
+    a = a > c ? a : c;
+  }
   return a > b ? a : b;
 }
 
@@ -167,9 +176,10 @@ FP8BL_EXPORT int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const 
   int st = validate_linear(x, q, scale_inv, y, m, n, k, path);
   if (st != FP8BL_OK) return st;
   if (m == 0 || n == 0) return FP8BL_OK;
-  const bool skinny = path == FP8BL_PATH_SKINNY || (path == FP8BL_PATH_AUTO && m <= kSkinnyMaxM);
-  const size_t need = skinny ? fp8bl::skinny_workspace_bytes(m, n, k)
-                             : fp8bl::tiled_workspace_bytes(m, n, k);
+  if (path == FP8BL_PATH_AUTO) path = m <= kSkinnyMaxM ? FP8BL_PATH_SKINNY : FP8BL_PATH_TILED;
+  const size_t need = path == FP8BL_PATH_SKINNY ? fp8bl::skinny_workspace_bytes(m, n, k)
+                    : path == FP8BL_PATH_LARGE  ? fp8bl::large_workspace_bytes(m, n, k)
+                                                : fp8bl::tiled_workspace_bytes(m, n, k);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return FP8BL_WORKSPACE;
     if (!aligned(workspace, fp8bl::kWorkspaceAlign)) return FP8BL_ALIGNMENT;
@@ -181,9 +191,12 @@ FP8BL_EXPORT int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const 
   }
   st = gate_current_device();
   if (st != FP8BL_OK) return st;
-  const hipError_t e = skinny
-      ? fp8bl::launch_gemm_skinny(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream)
-      : fp8bl::launch_gemm_tiled(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream);
+  const hipError_t e =
+      path == FP8BL_PATH_SKINNY
+          ? fp8bl::launch_gemm_skinny(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream)
+      : path == FP8BL_PATH_LARGE
+          ? fp8bl::launch_gemm_large(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream)
+          : fp8bl::launch_gemm_tiled(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream);
   return hip_status(e);
 }
 

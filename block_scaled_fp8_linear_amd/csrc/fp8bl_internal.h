@@ -31,6 +31,17 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
                              uint16_t* y, int64_t m, int64_t n, int64_t k,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Large-M fused GEMM: 256x256 tiles of four waves, X through a three-stage
+// direct-to-LDS ring, codes decoded one sub-step ahead of the MFMAs.
+struct LargePlan {
+  int splits, kt_per_split;
+};
+LargePlan plan_large(int64_t m, int64_t n, int64_t k);
+size_t large_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_large(const uint16_t* x, const uint8_t* q, const float* s,
+                             uint16_t* y, int64_t m, int64_t n, int64_t k,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 // MLP gate/up pair with the SwiGLU epilogue: h = swiglu(x Wg^T, x Wu^T).
 hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
                               const uint8_t* qu, const float* su, uint16_t* h,

@@ -27,7 +27,7 @@ pytestmark = [
 
 import block_scaled_fp8_linear_amd as F  # noqa: E402
 
-PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY}
+PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY, "large": F.PATH_LARGE}
 
 
 def run_linear(x_bits, q, s, path=F.PATH_AUTO):
@@ -250,7 +250,24 @@ def test_linear_square_tile_shapes(m, n, k):
     assert_bound(y, yr, ar, f"square tile {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("m,n,k", [
+    (256, 256, 64), (300, 520, 1040), (513, 300, 4112), (100, 700, 5200),
+    (257, 1000, 2576), (1000, 300, 784), (600, 2048, 3072), (40, 130, 16), (2304, 2560, 512),
+])
+def test_linear_large_tile_shapes(m, n, k):
+    """The 256x256 four-wave kernel forced on shapes with partial tiles in M
+    and N, K tails inside a 64-wide step and a 16-wide sub-step, N % 4 != 0
+    (element stores), 8 and 4 K splits (100x700x5200, 257x1000x2576) and
+    more tiles than CUs. Full compare against the oracle."""
+    x, w = random_problem(m * 3 + n * 11 + k, m, n, k)
+    q, s = O.quantize(w)
+    say("linear large tile", m, n, k)
+    y = run_linear(x, q, s, F.PATH_LARGE)
+    yr, ar = O.linear_exact(x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"large tile {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
 def test_linear_tiny_workload(path):
     lin = generate("tiny").linears[0]
     q, s = O.quantize(lin.w)
@@ -260,7 +277,7 @@ def test_linear_tiny_workload(path):
     assert_bound(y, yr, ar, f"tiny {path}")
 
 
-@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
 def test_linear_one_hot_identity(path):
     """X = I (M = K = 256): every output is a single exact product, so Y must
     equal W_hat^T bit for bit: the GEMM consumes exactly the dequant's bf16."""
@@ -273,7 +290,7 @@ def test_linear_one_hot_identity(path):
     assert np.array_equal(y, O.dequant(q, s).T)
 
 
-@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
 def test_linear_zero_input_gives_positive_zero(path):
     _, w = random_problem(3, 1, 300, 512)
     q, s = O.quantize(w)
@@ -283,7 +300,7 @@ def test_linear_zero_input_gives_positive_zero(path):
     assert np.all(y == 0)
 
 
-@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
 def test_linear_power_of_two_scaling_is_exact(path):
     x, w = random_problem(12, 48, 320, 768)
     q, s = O.quantize(w)
@@ -294,7 +311,7 @@ def test_linear_power_of_two_scaling_is_exact(path):
     assert np.array_equal(O.bf16_rne_bits(O.bf16_bits_to_f32(y1) * np.float32(4.0)), y2)
 
 
-@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
 def test_linear_reproducible(path):
     x, w = random_problem(44, 24, 1000, 4096)
     q, s = O.quantize(w)
@@ -348,7 +365,7 @@ def test_linear_graph_replay_matches_eager(m, n, k):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path", ["tiled", "skinny"])
+@pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
 def test_linear_largest_k_sampled(path):
     """K at the interface's limit (2^20): 16384 tiled K steps or 4096 skinny
     super-steps, 8192 scale blocks per row; outputs sampled against Y*."""
