@@ -9,6 +9,7 @@ hand-written HIP) provides:
 * ``fp8_block_quantize(w)``  -> (q, s)     the converter's quantization (fp32 or bf16 w)
 * ``fp8_block_dequant(q, s)`` -> bf16 W_hat  bit-exact dequant
 * ``fp8_block_linear(x, q, s)`` -> bf16 Y = X W_hat^T, fp32 accumulation
+  (``fp8_block_linear_noalloc(x, q, s, out)``: the same with no allocation)
 * ``fp8_block_mlp_gate_up(x, qg, sg, qu, su)`` -> bf16 swiglu(X Wg^T, X Wu^T)
   in one launch (the MLP's gate/up pair)
 * ``fp8_act_quantize(x)`` -> (xq, x_scale)  per-token 1x128 activation quantizer
@@ -42,6 +43,7 @@ BLOCK = 128
 __all__ = [
     "fp8_block_quantize", "fp8_block_dequant", "fp8_block_linear", "fp8_block_mlp_gate_up",
     "fp8_act_quantize", "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16",
+    "fp8_block_linear_noalloc",
     "workspace_size", "w8a8_workspace_size",
     "device_supported", "abi_version", "status_string", "Fp8blError",
     "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "PATH_LARGE", "scale_grid_shape", "fp8_block_stream_read",
@@ -142,6 +144,31 @@ def fp8_block_linear(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
         _check(_lib.linear_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), out.data_ptr(),
                                m, n, k, ws_ptr, ws_bytes, path, _stream(x.device)),
                "fp8_block_linear")
+    return out
+
+
+def fp8_block_linear_noalloc(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
+                             out: torch.Tensor) -> torch.Tensor:
+    """fp8_block_linear into a caller-given ``out``, with the split-K partials
+    in the library's own per-device scratch (64 MiB): nothing is allocated,
+    here or in the library. Calls on one device share that scratch and must
+    be ordered (one stream)."""
+    _need(x, torch.bfloat16, "x")
+    _need(q, torch.uint8, "q")
+    _need(s, torch.float32, "s")
+    _need(out, torch.bfloat16, "out")
+    m, k = x.shape
+    n, kq = q.shape
+    if kq != k:
+        raise ValueError(f"K mismatch: x has {k}, q has {kq}")
+    if tuple(s.shape) != scale_grid_shape(n, k):
+        raise ValueError(f"scale grid must be {scale_grid_shape(n, k)}, got {tuple(s.shape)}")
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out shape")
+    with torch.cuda.device(x.device):
+        _check(_lib.linear_noalloc_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), out.data_ptr(),
+                                       m, n, k, _stream(x.device)),
+               "fp8_block_linear_noalloc")
     return out
 
 

@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
     lib.fp8_block_linear_ex.restype = c_int
     lib.fp8_block_linear_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, c_int, vp]
+    lib.fp8_block_linear_noalloc.restype = c_int
+    lib.fp8_block_linear_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_block_mlp_gate_up.restype = c_int
     lib.fp8_block_mlp_gate_up.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_act_quantize.restype = c_int
@@ -113,6 +115,14 @@ def dequant_raw(q: int, s: int, w: int, n: int, k: int, stream: int = 0) -> int:
 def linear_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,
                ws: int, ws_bytes: int, path: int = PATH_AUTO, stream: int = 0) -> int:
     return load().fp8_block_linear_ex(x, q, s, y, m, n, k, ws, ws_bytes, path, stream)
+
+
+def linear_noalloc_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,
+                       stream: int = 0) -> int:
+    return load().fp8_block_linear_noalloc(x, q, s, y, m, n, k, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 def mlp_gate_up_raw(x: int, qg: int, sg: int, qu: int, su: int, h: int,

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "fp8bl_internal.h"
 
@@ -169,6 +170,64 @@ FP8BL_EXPORT size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_
   return a > b ? a : b;
 }
 
+namespace {
+
+// The kernel a call runs: the forced one, or the library's choice for AUTO.
+int resolve_path(int path, int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
+  if (path != FP8BL_PATH_AUTO) return path;
+  return m <= kSkinnyMaxM ? FP8BL_PATH_SKINNY : FP8BL_PATH_TILED;
+}
+
+// Split-K partial bytes of one (resolved) path on one shape.
+size_t path_workspace_bytes(int path, int64_t m, int64_t n, int64_t k) {
+  return path == FP8BL_PATH_SKINNY ? fp8bl::skinny_workspace_bytes(m, n, k)
+       : path == FP8BL_PATH_LARGE  ? fp8bl::large_workspace_bytes(m, n, k)
+                                   : fp8bl::tiled_workspace_bytes(m, n, k);
+}
+
+hipError_t launch_linear(int path, const uint16_t* x, const uint8_t* q, const float* s, uint16_t* y,
+                         int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  return path == FP8BL_PATH_SKINNY
+             ? fp8bl::launch_gemm_skinny(x, q, s, y, m, n, k, ws, ws_bytes, stream)
+         : path == FP8BL_PATH_LARGE
+             ? fp8bl::launch_gemm_large(x, q, s, y, m, n, k, ws, ws_bytes, stream)
+             : fp8bl::launch_gemm_tiled(x, q, s, y, m, n, k, ws, ws_bytes, stream);
+}
+
+// ---- Library-held scratch for fp8_block_linear_noalloc.
+// One copy of this array per device (the code object's global), kept until
+// the process ends. Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, looked up once per device on
+// the first call there, with that device current.
+constexpr size_t kScratchBytes = (size_t)FP8BL_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8BL_HIP_ERROR;
+  if (dev < 0 || dev >= kMaxDevices) return FP8BL_UNSUPPORTED_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return FP8BL_HIP_ERROR;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8BL_OK;
+}
+
+}  // namespace
+
 FP8BL_EXPORT int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_inv,
                                      uint16_t* y, int64_t m, int64_t n, int64_t k,
                                      void* workspace, size_t workspace_bytes, int path,
@@ -176,10 +235,8 @@ FP8BL_EXPORT int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const 
   int st = validate_linear(x, q, scale_inv, y, m, n, k, path);
   if (st != FP8BL_OK) return st;
   if (m == 0 || n == 0) return FP8BL_OK;
-  if (path == FP8BL_PATH_AUTO) path = m <= kSkinnyMaxM ? FP8BL_PATH_SKINNY : FP8BL_PATH_TILED;
-  const size_t need = path == FP8BL_PATH_SKINNY ? fp8bl::skinny_workspace_bytes(m, n, k)
-                    : path == FP8BL_PATH_LARGE  ? fp8bl::large_workspace_bytes(m, n, k)
-                                                : fp8bl::tiled_workspace_bytes(m, n, k);
+  path = resolve_path(path, m, n, k);
+  const size_t need = path_workspace_bytes(path, m, n, k);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return FP8BL_WORKSPACE;
     if (!aligned(workspace, fp8bl::kWorkspaceAlign)) return FP8BL_ALIGNMENT;
@@ -191,13 +248,29 @@ FP8BL_EXPORT int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const 
   }
   st = gate_current_device();
   if (st != FP8BL_OK) return st;
-  const hipError_t e =
-      path == FP8BL_PATH_SKINNY
-          ? fp8bl::launch_gemm_skinny(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream)
-      : path == FP8BL_PATH_LARGE
-          ? fp8bl::launch_gemm_large(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream)
-          : fp8bl::launch_gemm_tiled(x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream);
-  return hip_status(e);
+  return hip_status(launch_linear(path, x, q, scale_inv, y, m, n, k, workspace, workspace_bytes, stream));
+}
+
+FP8BL_EXPORT int fp8_block_linear_noalloc(const uint16_t* x, const uint8_t* q,
+                                          const float* scale_inv, uint16_t* y, int64_t m,
+                                          int64_t n, int64_t k, hipStream_t stream) {
+  int st = validate_linear(x, q, scale_inv, y, m, n, k, FP8BL_PATH_AUTO);
+  if (st != FP8BL_OK) return st;
+  if (m == 0 || n == 0) return FP8BL_OK;
+  const int path = resolve_path(FP8BL_PATH_AUTO, m, n, k);
+  const size_t need = path_workspace_bytes(path, m, n, k);
+  if (need > kScratchBytes) return FP8BL_WORKSPACE;
+  st = gate_current_device();
+  if (st != FP8BL_OK) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = current_scratch(&ws);
+    if (st != FP8BL_OK) return st;
+  }
+  // The partials of every split are written in full before the reduce reads
+  // them, so the scratch needs no clearing between calls.
+  return hip_status(launch_linear(path, x, q, scale_inv, y, m, n, k, ws, need > 0 ? kScratchBytes : 0,
+                                  stream));
 }
 
 FP8BL_EXPORT int fp8_block_linear(const uint16_t* x, const uint8_t* q, const float* scale_inv,

@@ -26,7 +26,8 @@
  *     launched; no exception or abort crosses this interface. A fault inside a
  *     kernel surfaces, as in HIP, at the caller's next synchronisation.
  *   - The library keeps no state besides a per-device cached architecture
- *     check; calls on different streams may run concurrently.
+ *     check and the scratch of fp8_block_linear_noalloc; calls on different
+ *     streams may run concurrently (fp8_block_linear_noalloc excepted).
  *   - Scales are expected finite; other scales still follow the dequant
  *     formula (NaN products become the canonical bf16 NaN 0x7FC0).
  */
@@ -116,6 +117,29 @@ int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_
                         uint16_t* y, int64_t m, int64_t n, int64_t k,
                         void* workspace, size_t workspace_bytes, int path,
                         hipStream_t stream);
+
+/* Size of the scratch array fp8_block_linear_noalloc keeps on each device. */
+#define FP8BL_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* fp8_block_linear for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same operation, arguments and error codes as fp8_block_linear
+ * (AUTO path), except that the split-K partials go to a scratch array inside
+ * the library instead of a caller workspace:
+ *   - the scratch is FP8BL_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory
+ *     per device, part of the library's code object, held until the process
+ *     ends; the call allocates nothing (no hipMalloc, no hipFree);
+ *   - a shape whose partials need more than that returns FP8BL_WORKSPACE
+ *     before anything is launched (every shape with
+ *     fp8_block_linear_workspace_size <= 64 MiB fits);
+ *   - the first call on a device looks up the scratch's device address once
+ *     (hipGetSymbolAddress), with that device current;
+ *   - every call on a device shares that device's scratch, which keeps the
+ *     last call's partials (nothing in it needs clearing): calls that overlap
+ *     on one device (other streams, other host threads) race. Order them on
+ *     one stream. */
+int fp8_block_linear_noalloc(const uint16_t* x, const uint8_t* q, const float* scale_inv,
+                             uint16_t* y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 /* The MLP gate/up pair in one launch, with the SwiGLU epilogue (the step
  * after the gate and up linears; FastVideo fasth3_omniref_b200 README, "What

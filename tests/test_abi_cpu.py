@@ -22,6 +22,7 @@ def test_header_symbols_exported(lib):
         "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
         "fp8_block_mlp_gate_up", "fp8_act_quantize", "fp8_block_linear_w8a8_workspace_size",
         "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16", "fp8_block_stream_read",
+        "fp8_block_linear_noalloc",
     }
     for name in names:
         assert hasattr(lib, name), name
@@ -76,6 +77,31 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced here
 def test_linear_argument_errors(lib, args, status):
     x, q, s, y, m, n, k, ws, wsb, path = args
     assert L.linear_raw(x, q, s, y, m, n, k, ws, wsb, path) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (x, q, s, y, m, n, k)
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 4, 8, 15), L.FP8BL_INVALID_ARG),        # K % 16
+    ((0, FAKE, FAKE, 4 * FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),           # null x
+    ((FAKE, FAKE, FAKE, 0, 4, 8, 16), L.FP8BL_INVALID_ARG),               # null y
+    ((FAKE + 2, FAKE, FAKE, 4 * FAKE, 4, 8, 16), L.FP8BL_ALIGNMENT),      # x misaligned
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 16), L.FP8BL_INVALID_ARG),            # y overlaps x
+    ((FAKE, FAKE, FAKE, 4 * FAKE, 0, 8, 16), L.FP8BL_OK),                 # empty M: no-op
+    ((0, 0, 0, 0, 4, 0, 16), L.FP8BL_OK),                                 # empty N, null ok
+    # partials of 768 x 8192 x 65536 (split K) exceed the 64 MiB scratch
+    ((1 << 40, 1 << 41, 1 << 42, 1 << 43, 768, 8192, 65536), L.FP8BL_WORKSPACE),
+])
+def test_linear_noalloc_argument_errors(lib, args, status):
+    """The allocation-free linear checks its arguments like fp8_block_linear and
+    rejects a shape whose split-K partials exceed its scratch, all before any
+    HIP call (none of these touches a device)."""
+    assert L.linear_noalloc_raw(*args) == status
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(L.HEADER_PATH).read()
+    assert "#define FP8BL_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in text
+    assert L.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
 
 
 @pytest.mark.parametrize("args,status", [
