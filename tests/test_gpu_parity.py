@@ -27,7 +27,8 @@ pytestmark = [
 
 import block_scaled_fp8_linear_amd as F  # noqa: E402
 
-PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY, "large": F.PATH_LARGE}
+PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY, "large": F.PATH_LARGE,
+         "stream": F.PATH_STREAM}
 
 
 def run_linear(x_bits, q, s, path=F.PATH_AUTO):
@@ -215,6 +216,12 @@ def test_linear_small_shapes(m, n, k, path):
     x, w = random_problem(m * 131 + n * 7 + k, m, n, k)
     q, s = O.quantize(w)
     say("linear", path, m, n, k)
+    if path == "stream" and m > 32:
+        # the streaming kernel takes M <= 32: refused before any launch
+        with pytest.raises(F.Fp8blError) as e:
+            run_linear(x, q, s, PATHS[path])
+        assert e.value.status == F._lib.FP8BL_INVALID_ARG
+        return
     y = run_linear(x, q, s, PATHS[path])
     yr, ar = O.linear_exact(x, O.dequant(q, s))
     assert_bound(y, yr, ar, f"{path} {m}x{n}x{k}")
@@ -265,6 +272,65 @@ def test_linear_large_tile_shapes(m, n, k):
     y = run_linear(x, q, s, F.PATH_LARGE)
     yr, ar = O.linear_exact(x, O.dequant(q, s))
     assert_bound(y, yr, ar, f"large tile {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 8000, 8192), (16, 8000, 8192), (32, 8000, 8192), (5, 300, 5200), (16, 1000, 16),
+    (13, 4100, 4112), (16, 33, 2576), (2, 7, 1040), (24, 6000, 2048), (9, 520, 12304),
+    (17, 700, 9216), (32, 96, 3072),
+])
+def test_linear_stream_shapes(m, n, k):
+    """The chunked streaming kernel (M <= 32) forced on the skinny workload
+    shapes (M = 1, 16, 32), K tails inside a 1024-wide chunk (5200, 4112,
+    12304), K = 16 (one live chunk column), N below one 16-row tile and a
+    partial second tile, one and two M tiles, chunk counts with a fixed
+    unrolled schedule (1..8) and with the general loop (9, 13). Full compare
+    against the oracle."""
+    x, w = random_problem(m * 7 + n * 5 + k, m, n, k)
+    q, s = O.quantize(w)
+    say("linear stream", m, n, k)
+    y = run_linear(x, q, s, F.PATH_STREAM)
+    yr, ar = O.linear_exact(x, O.dequant(q, s))
+    assert_bound(y, yr, ar, f"stream {m}x{n}x{k}")
+
+
+def test_linear_stream_invariants():
+    """Streaming kernel: one-hot rows give W_hat columns bit for bit; zero X
+    gives +0; scaling X by 4 scales Y by 4 exactly; three runs agree bit for
+    bit."""
+    _, w = random_problem(91, 1, 300, 256)
+    q, s = O.quantize(w)
+    x = np.zeros((16, 256), dtype=np.uint16)
+    x[np.arange(16), 17 * np.arange(16)] = 0x3F80                 # bf16 1.0
+    say("stream one-hot")
+    y = run_linear(x, q, s, F.PATH_STREAM)
+    assert np.array_equal(y, O.dequant(q, s)[:, 17 * np.arange(16)].T)
+    say("stream zero input")
+    assert np.all(run_linear(np.zeros((16, 256), np.uint16), q, s, F.PATH_STREAM) == 0)
+    x, w = random_problem(92, 11, 700, 3072)
+    q, s = O.quantize(w)
+    x4 = O.bf16_rne_bits(O.bf16_bits_to_f32(x) * np.float32(4.0))
+    say("stream power-of-two scaling and reproducibility")
+    y1 = run_linear(x, q, s, F.PATH_STREAM)
+    assert np.array_equal(O.bf16_rne_bits(O.bf16_bits_to_f32(y1) * np.float32(4.0)),
+                          run_linear(x4, q, s, F.PATH_STREAM))
+    for _ in range(2):
+        assert np.array_equal(run_linear(x, q, s, F.PATH_STREAM), y1)
+
+
+def test_linear_stream_largest_k_sampled():
+    """K = 2^20 on the streaming kernel: 1024 chunks through the general loop."""
+    m, n, k = 16, 256, 1 << 20
+    rng = np.random.default_rng(39)
+    x = O.bf16_rne_bits(rng.standard_normal((m, k), dtype=np.float32)) & np.uint16(0xFFFF)
+    w = (rng.standard_normal((n, k), dtype=np.float32) * 0.02).astype(np.float32)
+    q, s = O.quantize(w)
+    say("largest K stream", m, n, k)
+    y = run_linear(x, q, s, F.PATH_STREAM)
+    ms = np.array([0, 7, 15]); ns = np.array([0, 255, 128, 3, 31, 32])
+    mm, nn = np.meshgrid(ms, ns, indexing="ij")
+    yr, ar = O.linear_sampled(x, q, s, mm.ravel(), nn.ravel())
+    assert_bound(y[mm.ravel(), nn.ravel()], yr, ar, "largest K stream")
 
 
 @pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
