@@ -49,7 +49,7 @@ WORKLOADS = {
 SECONDARY = ("skinny_m16", "skinny_m1")
 
 # --path values -> fp8bl_path
-PATHS = {"auto": 0, "tiled": 1, "skinny": 2, "large": 3, "stream": 4}
+PATHS = {"auto": 0, "tiled": 1, "skinny": 2, "large": 3}
 
 
 # What one timed launch (one library call per step) runs on the GPU; the

@@ -34,7 +34,7 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    PATH_AUTO, PATH_LARGE, PATH_SKINNY, PATH_STREAM, PATH_TILED, Fp8blError, abi_version, device_supported,
+    PATH_AUTO, PATH_LARGE, PATH_SKINNY, PATH_TILED, Fp8blError, abi_version, device_supported,
     status_string, w8a8_workspace_size, workspace_size,
 )
 
@@ -46,7 +46,7 @@ __all__ = [
     "fp8_block_linear_noalloc",
     "workspace_size", "w8a8_workspace_size",
     "device_supported", "abi_version", "status_string", "Fp8blError",
-    "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "PATH_LARGE", "PATH_STREAM", "scale_grid_shape", "fp8_block_stream_read",
+    "PATH_AUTO", "PATH_TILED", "PATH_SKINNY", "PATH_LARGE", "scale_grid_shape", "fp8_block_stream_read",
 ]
 
 

@@ -26,7 +26,6 @@ PATH_AUTO = 0
 PATH_TILED = 1
 PATH_SKINNY = 2
 PATH_LARGE = 3
-PATH_STREAM = 4
 
 _lib = None
 

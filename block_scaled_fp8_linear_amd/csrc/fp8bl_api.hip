@@ -66,10 +66,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP8BL_OK : FP8BL_HIP_ERR
 int validate_linear(const uint16_t* x, const uint8_t* q, const float* s, const uint16_t* y,
                     int64_t m, int64_t n, int64_t k, int path) {
   if (path != FP8BL_PATH_AUTO && path != FP8BL_PATH_TILED && path != FP8BL_PATH_SKINNY &&
-      path != FP8BL_PATH_LARGE && path != FP8BL_PATH_STREAM)
+      path != FP8BL_PATH_LARGE)
     return FP8BL_INVALID_ARG;
   if (path == FP8BL_PATH_LARGE && n >= kLargeMaxN) return FP8BL_INVALID_ARG;
-  if (path == FP8BL_PATH_STREAM && m > fp8bl::kStreamMaxM) return FP8BL_INVALID_ARG;
   if (m < 0 || m >= kMaxDim) return FP8BL_INVALID_ARG;
   int st = check_nk(n, k);
   if (st != FP8BL_OK) return st;
@@ -175,16 +174,16 @@ namespace {
 
 // The kernel a call runs: the forced one, or the library's choice for AUTO.
 int resolve_path(int path, int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
   if (path != FP8BL_PATH_AUTO) return path;
-  if (m > kSkinnyMaxM) return FP8BL_PATH_TILED;
-  return fp8bl::stream_preferred(m, n, k) ? FP8BL_PATH_STREAM : FP8BL_PATH_SKINNY;
+  return m <= kSkinnyMaxM ? FP8BL_PATH_SKINNY : FP8BL_PATH_TILED;
 }
 
 // Split-K partial bytes of one (resolved) path on one shape.
 size_t path_workspace_bytes(int path, int64_t m, int64_t n, int64_t k) {
   return path == FP8BL_PATH_SKINNY ? fp8bl::skinny_workspace_bytes(m, n, k)
        : path == FP8BL_PATH_LARGE  ? fp8bl::large_workspace_bytes(m, n, k)
-       : path == FP8BL_PATH_STREAM ? 0
                                    : fp8bl::tiled_workspace_bytes(m, n, k);
 }
 
@@ -193,8 +192,6 @@ hipError_t launch_linear(int path, const uint16_t* x, const uint8_t* q, const fl
                          hipStream_t stream) {
   return path == FP8BL_PATH_SKINNY
              ? fp8bl::launch_gemm_skinny(x, q, s, y, m, n, k, ws, ws_bytes, stream)
-         : path == FP8BL_PATH_STREAM
-             ? fp8bl::launch_gemm_stream(x, q, s, y, m, n, k, stream)
          : path == FP8BL_PATH_LARGE
              ? fp8bl::launch_gemm_large(x, q, s, y, m, n, k, ws, ws_bytes, stream)
              : fp8bl::launch_gemm_tiled(x, q, s, y, m, n, k, ws, ws_bytes, stream);

@@ -47,15 +47,6 @@ hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float*
                               const uint8_t* qu, const float* su, uint16_t* h,
                               int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
-// Skinny-M streaming GEMM for M <= 32: eight waves per 32 weight rows, the
-// weight streamed in 1024-column chunks through a four-slot direct-to-LDS
-// ring; no workspace.
-constexpr int64_t kStreamMaxM = 32;
-hipError_t launch_gemm_stream(const uint16_t* x, const uint8_t* q, const float* s,
-                              uint16_t* y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
-// Whether the library's own choice for M <= 32 is the streaming kernel.
-bool stream_preferred(int64_t m, int64_t n, int64_t k);
-
 // Skinny-M (M <= 32 rows per pass) weight-streaming GEMM.
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* s,

@@ -52,6 +52,14 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// The weight is read once: its loads carry the non-temporal cache policy
+// (bit 1 of the buffer instruction's cache field on gfx950), which on MI355X
+// streams an 8000 x 8192 weight 5-10% faster than default-policy loads.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
+
 template <int MT, int NT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64)
 void gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
@@ -123,7 +131,7 @@ void gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
       const int row = 4 * r + lrow4;
       const bool kin = live && (int)kb + ((lchk ^ row) * 16) < K;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) w[j][r] = buf_load16(wrs, kin ? woff[j][r] + kb : kOob);
+      for (int j = 0; j < NT; ++j) w[j][r] = buf_load16_nt(wrs, kin ? woff[j][r] + kb : kOob);
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -277,195 +285,6 @@ void reduce_partials_kernel(const float* __restrict__ part, uint16_t* __restrict
   }
 }
 
-// ---------------------------------------------------------------------------
-// Streaming kernel for M <= 32 when the weight has enough rows to give every
-// CU a workgroup. It is organised around the weight stream alone: each
-// workgroup reads its 32 weight rows (a contiguous 32*K-byte region) in
-// chunks of 1024 columns, each row's 1 KB of a chunk by one 16-byte-per-lane
-// instruction, non-temporal, straight into LDS; a four-slot ring keeps three
-// chunks (96 KB) in flight per workgroup while the fourth is consumed. On
-// MI355X a loads-only probe of this access pattern over an 8000 x 8192
-// weight streams at 5.8-5.9 TB/s, against 5.0-5.3 TB/s for the same loads
-// without the non-temporal hint and 5.5 TB/s for 512-byte row pieces.
-//
-// Workgroup: eight waves. Wave w loads rows 4w .. 4w+3 of every chunk and,
-// after the chunk's barrier, computes K columns [128w, 128w + 128) of the
-// chunk for both 16-row tiles (its columns lie in one 128-wide scale block).
-// One barrier per chunk: when every wave has its own loads of chunk c and
-// has passed the barrier, chunk c is complete in LDS and chunk c - 1 is no
-// longer read, so its slot is refilled with chunk c + 3 before chunk c is
-// computed. X (from L2) rides the same ring in registers: the X of chunk c
-// is loaded with its codes, so a single vmcnt wait covers both.
-//
-// LDS slot: row r at r * 1024 bytes; logical 16-byte chunk j of a row sits
-// at physical chunk j ^ (r % 16) (the swizzle is applied on the global side:
-// lane l fetches logical chunk l ^ (r % 16) and the hardware writes it at
-// physical chunk l), so the operand reads below (16 lanes on 16 rows, one
-// logical chunk) hit 16 distinct 16-byte bank groups.
-//
-// K order (a permutation shared by A and B): read e of wave w gives lane
-// group g the codes of logical chunk 8w + 4e + g; its 16 codes feed two
-// MFMAs (h = 0, 1: 8 codes each) and X is loaded with the same k.
-//
-// v_mfma_f32_16x16x32_bf16 with X as A and the decoded weight as B: lane l
-// ends with Y rows 4(l/16) + j, j = 0..3, of column l % 16 of its tile. The
-// eight waves' sums meet in LDS (in the ring, once the stream is drained)
-// and are added in wave order; one bf16 rounding per output, no split-K.
-constexpr int kCoWaves = 8;
-constexpr int kCoRows = 32;                        // weight rows per workgroup
-constexpr int kCoChunk = 1024;                     // K per chunk
-constexpr int kCoSlots = 4;                        // ring depth
-constexpr int kCoSlot = kCoRows * kCoChunk;        // 32 KB
-constexpr int kCoRowsPerWave = kCoRows / kCoWaves; // rows each wave loads (4)
-constexpr int kCoSub = kCoChunk / kCoWaves;        // K each wave computes per chunk (128)
-constexpr int kNonTemporal = 2;                    // buffer cache policy bit: streamed once
-
-static_assert(kCoSub == kBlock, "a wave's columns of a chunk form one scale block");
-
-// s_waitcnt immediates (gfx9: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4],
-// lgkmcnt[11:8]): vm_wait(n) waits until at most n vector-memory operations
-// of this wave are outstanding and ignores the other counters.
-constexpr int co_vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-typedef __attribute__((address_space(3))) void* co_lds_ptr_t;
-
-template <int MT, int NCH>
-__global__ __launch_bounds__(kCoWaves * 64, 1)
-void gemm_stream_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
-                        const float* __restrict__ s, uint16_t* __restrict__ y,
-                        int M, int N, int K, int gk, int nchunks) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kCoSlots][kCoSlot];
-
-  constexpr int kXLoads = MT * 4;                    // 16-byte X loads per lane per chunk
-  constexpr int kPerChunk = kCoRowsPerWave + kXLoads;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * kCoRows;
-
-  const __amdgpu_buffer_rsrc_t wrs =
-      make_rsrc(q + (size_t)n0 * K, (uint32_t)(min(N - n0, kCoRows) * K));
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)(M * K * 2));
-  const int xm = lane & 15;                          // X row within an M tile / weight row in a tile
-  const int xg = lane >> 4;                          // lane group
-
-  // Chunk c's loads into ring slot `slot` and X registers xr.
-  auto issue = [&](int c, int slot, u32x4 (&xr)[MT][2][2]) {
-    const int kb = c * kCoChunk;
-#pragma unroll
-    for (int j = 0; j < kCoRowsPerWave; ++j) {
-      const int row = kCoRowsPerWave * wave + j;
-      const int k = kb + 16 * (lane ^ (row & 15));
-      const uint32_t off = k < K ? (uint32_t)(row * K + k) : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (co_lds_ptr_t)&ring[slot][row * kCoChunk], 16,
-                                               off, 0, 0, kNonTemporal);
-    }
-    const int ks = kb + kCoSub * wave;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k = ks + 16 * (4 * e + xg);
-        const uint32_t o = (uint32_t)(((16 * mt + xm) * K + k) * 2);
-        xr[mt][e][0] = buf_load16(xrs, k < K ? o : kOob);
-        xr[mt][e][1] = buf_load16(xrs, k < K ? o + 16 : kOob);
-      }
-  };
-
-  f32x4 acc[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* srow = s + (size_t)(n0 / kBlock) * gk;
-
-  auto compute = [&](int c, int slot, const u32x4 (&xr)[MT][2][2]) {
-    const int kblk = c * (kCoChunk / kBlock) + wave;
-    const float sc = kblk < gk ? srow[kblk] : 0.0f;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int phys = (8 * wave + 4 * e + xg) ^ xm;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(&ring[slot][(16 * t + xm) * kCoChunk + phys * 16]);
-        const bf16x8 w0 = dequant8(cw[0], cw[1], sc);
-        const bf16x8 w1 = dequant8(cw[2], cw[3], sc);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, xr[mt][e][0]), w0, acc[mt][t], 0, 0, 0);
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, xr[mt][e][1]), w1, acc[mt][t], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  u32x4 x0[MT][2][2], x1[MT][2][2], x2[MT][2][2], x3[MT][2][2];
-  // With the chunk count fixed at compile time (NCH > 0) the loop below is
-  // straight-line code: the compiler then tracks which loads the X registers
-  // wait for exactly, and chunks past the end are never issued. NCH == 0 is
-  // the general loop (chunks past the end read nothing).
-  const int n = NCH > 0 ? NCH : nchunks;
-  issue(0, 0, x0);
-  if (NCH == 0 || 1 < n) issue(1, 1, x1);
-  if (NCH == 0 || 2 < n) issue(2, 2, x2);
-
-  // Chunk c: its own loads landed (the chunks issued after it may still be
-  // in flight), barrier, refill the slot of chunk c-1 with chunk c+3,
-  // compute chunk c. The barrier is the bare s_barrier: a fenced one would
-  // also wait for the ring's loads still in flight. The LDS reads of chunk c
-  // are ordered after it by the wait (this wave's loads) and the barrier
-  // (every other wave's).
-  auto step = [&](int c, int slot, const u32x4 (&xc)[MT][2][2], u32x4 (&xn)[MT][2][2]) {
-    const int after = NCH > 0 ? min(2, NCH - 1 - c) : 2;    // chunks issued after c
-    if (after >= 2)
-      __builtin_amdgcn_s_waitcnt(co_vm_wait(2 * kPerChunk));
-    else if (after == 1)
-      __builtin_amdgcn_s_waitcnt(co_vm_wait(kPerChunk));
-    else
-      __builtin_amdgcn_s_waitcnt(co_vm_wait(0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (NCH == 0 || c + 3 < NCH) issue(c + 3, (slot + 3) & 3, xn);
-    compute(c, slot, xc);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-#pragma unroll
-  for (int c0 = 0; c0 < (NCH > 0 ? NCH : nchunks); c0 += 4) {
-    step(c0, 0, x0, x3);
-    if (c0 + 1 >= n) break;
-    step(c0 + 1, 1, x1, x0);
-    if (c0 + 2 >= n) break;
-    step(c0 + 2, 2, x2, x1);
-    if (c0 + 3 >= n) break;
-    step(c0 + 3, 3, x3, x2);
-  }
-  __builtin_amdgcn_s_waitcnt(co_vm_wait(0));
-  __syncthreads();
-
-  // Cross-wave sum in wave order, in the drained ring: one wave per
-  // (M tile, weight tile) pair finishes it.
-  f32x4* red = reinterpret_cast<f32x4*>(&ring[0][0]);   // [wave][pair][64]
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) red[(wave * 2 * MT + 2 * mt + t) * 64 + lane] = acc[mt][t];
-  __syncthreads();
-  if (wave >= 2 * MT) return;
-  const int mt = wave >> 1, t = wave & 1;
-  f32x4 sum = red[wave * 64 + lane];
-#pragma unroll
-  for (int w = 1; w < kCoWaves; ++w) {
-    const f32x4 o = red[(w * 2 * MT + wave) * 64 + lane];
-    sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
-  }
-  const int col = n0 + 16 * t + xm;
-  if (col >= N) return;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * mt + 4 * xg + j;
-    if (row < M) y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (__bf16)sum[j]);
-  }
-}
-
 constexpr int kWaves = 4;
 
 struct SkinnyPlan {
@@ -520,40 +339,6 @@ size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   const SkinnyPlan p = plan_skinny(rows, n, k);
   if (p.splits <= 1) return 0;
   return round_up((size_t)p.splits * partial_slab(rows, n) * sizeof(float), kWorkspaceAlign);
-}
-
-template <int MT>
-hipError_t launch_stream_mt(const uint16_t* x, const uint8_t* q, const float* s, uint16_t* y,
-                            int m, int n, int k, int gk, int nchunks, hipStream_t stream) {
-  const dim3 grid((uint32_t)((n + kCoRows - 1) / kCoRows)), block(kCoWaves * 64);
-  switch (nchunks) {
-#define FP8BL_CO_CASE(C) \
-    case C: hipLaunchKernelGGL((gemm_stream_kernel<MT, C>), grid, block, 0, stream, x, q, s, y, m, n, k, gk, nchunks); break;
-    FP8BL_CO_CASE(1) FP8BL_CO_CASE(2) FP8BL_CO_CASE(3) FP8BL_CO_CASE(4)
-    FP8BL_CO_CASE(5) FP8BL_CO_CASE(6) FP8BL_CO_CASE(7) FP8BL_CO_CASE(8)
-#undef FP8BL_CO_CASE
-    default:
-      hipLaunchKernelGGL((gemm_stream_kernel<MT, 0>), grid, block, 0, stream, x, q, s, y, m, n, k, gk, nchunks);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_stream(const uint16_t* x, const uint8_t* q, const float* s,
-                              uint16_t* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  if (m > kStreamMaxM) return hipErrorInvalidValue;
-  const int gk = (int)((k + kBlock - 1) / kBlock);
-  const int nchunks = (int)((k + kCoChunk - 1) / kCoChunk);
-  if (m <= 16) return launch_stream_mt<1>(x, q, s, y, (int)m, (int)n, (int)k, gk, nchunks, stream);
-  return launch_stream_mt<2>(x, q, s, y, (int)m, (int)n, (int)k, gk, nchunks, stream);
-}
-
-bool stream_preferred(int64_t m, int64_t n, int64_t k) {
-  // Not chosen yet: on 16 x 8000 x 8192 and 1 x 8000 x 8192 it measured
-  // 19.1 and 17.2 us against the split-K kernel's 18.7-19.2 and 16.3-16.8.
-  (void)m;
-  (void)n;
-  (void)k;
-  return false;
 }
 
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint8_t* q, const float* s,

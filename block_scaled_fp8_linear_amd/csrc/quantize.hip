@@ -23,11 +23,13 @@ constexpr int kThreads = 256;
 
 // Two fp32 values -> their E4M3FN codes in bytes 0 and 1 (HI false) or 2
 // and 3 (HI) of `old`, by the gfx950 conversion v_cvt_pk_fp8_f32: nearest
-// code, ties to even, sign kept (-0 -> 0x80). Over every fp32 pattern below
-// 464 in magnitude, both signs, it gives the same codes as an integer
-// nearest-even encoder that saturates at 448 (checked exhaustively on
-// MI355X). The quotients w / S and x / S of both quantizers stay below
-// 448 * (1 + 2^-23), where saturation and rounding to 448 coincide.
+// code, ties to even, sign kept (-0 -> 0x80). It gives the same codes as an
+// integer nearest-even encoder that saturates at 448 on every input the GPU
+// tests feed it: each bf16-valued fp32 up to 448 and each fp32 within 4096
+// ulp of every code and of every midpoint between neighbouring codes, both
+// signs, plus subnormal inputs. The quotients w / S and x / S of both
+// quantizers stay below 448 * (1 + 2^-23), where saturation and rounding to
+// 448 coincide.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_hw(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
@@ -106,8 +108,8 @@ void quantize_kernel(const T* __restrict__ w, uint8_t* __restrict__ q,
 // q0 = fl32(x * y), r = fma(-q0, S, x), q = fma(r, y, q0) carrying the sign
 // of x (for x = -0 the fma sum is +0). Over every finite bf16 x with
 // |x| <= amax and every bf16 amax whose S >= 2^-64, this gives the same E4M3
-// code as the IEEE quotient (checked exhaustively on MI355X, both signs);
-// smaller scales take the IEEE division.
+// code as the IEEE quotient (a GPU test runs every such pair, both signs,
+// against a plain CPU reference); smaller scales take the IEEE division.
 __global__ __launch_bounds__(kThreads)
 void act_quantize_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
                          float* __restrict__ xs, int M, int K) {

@@ -56,19 +56,16 @@ enum fp8bl_status {
   FP8BL_HIP_ERROR = 5           /* a HIP runtime call failed (device query or launch) */
 };
 
-/* Kernel choice for fp8_block_linear_ex. AUTO picks STREAM or SKINNY for
- * M <= 32 and one of the tiled kernels otherwise; the other values force a
- * kernel (for tests and measurements). TILED is the tile-planned kernel
- * (128- and 256-row tiles), LARGE the 256x256 four-wave kernel, which takes
- * shapes with N < 2^21, SKINNY the split-K weight-streaming kernel for
- * M <= 32 per pass and STREAM the chunked streaming kernel for M <= 32
- * (FP8BL_INVALID_ARG for shapes outside these limits). */
+/* Kernel choice for fp8_block_linear_ex. AUTO picks SKINNY for M <= 32 and
+ * one of the two tiled kernels otherwise; the other values force a kernel
+ * (for tests and measurements). TILED is the tile-planned kernel (128- and
+ * 256-row tiles), LARGE the 256x256 four-wave kernel, which takes shapes
+ * with N < 2^21 (FP8BL_INVALID_ARG otherwise). */
 enum fp8bl_path {
   FP8BL_PATH_AUTO = 0,
   FP8BL_PATH_TILED = 1,
   FP8BL_PATH_SKINNY = 2,
-  FP8BL_PATH_LARGE = 3,
-  FP8BL_PATH_STREAM = 4
+  FP8BL_PATH_LARGE = 3
 };
 
 /* Version of this interface (FP8BL_ABI_VERSION). */
@@ -115,8 +112,7 @@ int fp8_block_linear(const uint16_t* x, const uint8_t* q, const float* scale_inv
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* fp8_block_linear with an explicit path (enum fp8bl_path). Same contract;
- * every path accepts every shape, except LARGE, which needs N < 2^21, and
- * STREAM, which needs M <= 32. */
+ * every path accepts every shape, except LARGE, which needs N < 2^21. */
 int fp8_block_linear_ex(const uint16_t* x, const uint8_t* q, const float* scale_inv,
                         uint16_t* y, int64_t m, int64_t n, int64_t k,
                         void* workspace, size_t workspace_bytes, int path,

@@ -27,8 +27,7 @@ pytestmark = [
 
 import block_scaled_fp8_linear_amd as F  # noqa: E402
 
-PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY, "large": F.PATH_LARGE,
-         "stream": F.PATH_STREAM}
+PATHS = {"auto": F.PATH_AUTO, "tiled": F.PATH_TILED, "skinny": F.PATH_SKINNY, "large": F.PATH_LARGE}
 
 
 def run_linear(x_bits, q, s, path=F.PATH_AUTO):
@@ -194,6 +193,38 @@ def test_quantize_codes_around_every_midpoint():
     assert bad.size == 0, [(float(w[r, c]), int(u8(qt)[r, c]), int(q[r, c])) for r, c in bad[:8]]
 
 
+def test_quantize_hardware_encode_wide():
+    """The hardware E4M3 encode behind both quantizers, with S = 1 (every
+    block holds 448), against the oracle's integer nearest-even encoder:
+    every fp32 value that is a bf16 pattern up to 448 in magnitude, and every
+    fp32 pattern within 4096 ulp of each midpoint between neighbouring codes
+    and of each code, both signs (about 4.2 M inputs)."""
+    t = O.e4m3_table()[:0x7F]
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([mids, t.astype(np.float32)]).view(np.uint32).astype(np.int64)
+    near = (pts[:, None] + np.arange(-4096, 4097, dtype=np.int64)[None, :]).ravel()
+    near = near[(near >= 0) & (near < 0x7F800000)].astype(np.uint32)
+    bf = (np.arange(0, 0x7F80, dtype=np.uint32) << np.uint32(16))
+    mags = np.unique(np.concatenate([near, bf])).view(np.float32)
+    mags = mags[mags <= 448.0]
+    vals = np.concatenate([mags, -mags]).astype(np.float32)
+    rows = -(-vals.size // 254)
+    flat = np.zeros(rows * 254, dtype=np.float32)
+    flat[:vals.size] = vals
+    flat = flat.reshape(rows, 254)
+    w = np.zeros((rows, 256), dtype=np.float32)
+    w[:, 0] = w[:, 128] = 448.0                    # both column blocks hold amax 448 -> S = 1
+    w[:, 1:128], w[:, 129:] = flat[:, :127], flat[:, 127:]
+    say("quantize hardware encode, wide", w.shape, vals.size, "inputs")
+    qt, st = F.fp8_block_quantize(to_f32(w))
+    torch.cuda.synchronize()
+    q, s = O.quantize(w)
+    assert np.all(s == 1.0)
+    assert np.array_equal(f32(st).view(np.uint32), s.view(np.uint32))
+    bad = np.argwhere(u8(qt) != q)
+    assert bad.size == 0, [(float(w[r, c]), int(u8(qt)[r, c]), int(q[r, c])) for r, c in bad[:8]]
+
+
 # ---------------------------------------------------------------------------
 # linear: bound against the fp64 oracle, both kernels forced on small shapes
 # ---------------------------------------------------------------------------
@@ -216,12 +247,6 @@ def test_linear_small_shapes(m, n, k, path):
     x, w = random_problem(m * 131 + n * 7 + k, m, n, k)
     q, s = O.quantize(w)
     say("linear", path, m, n, k)
-    if path == "stream" and m > 32:
-        # the streaming kernel takes M <= 32: refused before any launch
-        with pytest.raises(F.Fp8blError) as e:
-            run_linear(x, q, s, PATHS[path])
-        assert e.value.status == F._lib.FP8BL_INVALID_ARG
-        return
     y = run_linear(x, q, s, PATHS[path])
     yr, ar = O.linear_exact(x, O.dequant(q, s))
     assert_bound(y, yr, ar, f"{path} {m}x{n}x{k}")
@@ -272,65 +297,6 @@ def test_linear_large_tile_shapes(m, n, k):
     y = run_linear(x, q, s, F.PATH_LARGE)
     yr, ar = O.linear_exact(x, O.dequant(q, s))
     assert_bound(y, yr, ar, f"large tile {m}x{n}x{k}")
-
-
-@pytest.mark.parametrize("m,n,k", [
-    (1, 8000, 8192), (16, 8000, 8192), (32, 8000, 8192), (5, 300, 5200), (16, 1000, 16),
-    (13, 4100, 4112), (16, 33, 2576), (2, 7, 1040), (24, 6000, 2048), (9, 520, 12304),
-    (17, 700, 9216), (32, 96, 3072),
-])
-def test_linear_stream_shapes(m, n, k):
-    """The chunked streaming kernel (M <= 32) forced on the skinny workload
-    shapes (M = 1, 16, 32), K tails inside a 1024-wide chunk (5200, 4112,
-    12304), K = 16 (one live chunk column), N below one 16-row tile and a
-    partial second tile, one and two M tiles, chunk counts with a fixed
-    unrolled schedule (1..8) and with the general loop (9, 13). Full compare
-    against the oracle."""
-    x, w = random_problem(m * 7 + n * 5 + k, m, n, k)
-    q, s = O.quantize(w)
-    say("linear stream", m, n, k)
-    y = run_linear(x, q, s, F.PATH_STREAM)
-    yr, ar = O.linear_exact(x, O.dequant(q, s))
-    assert_bound(y, yr, ar, f"stream {m}x{n}x{k}")
-
-
-def test_linear_stream_invariants():
-    """Streaming kernel: one-hot rows give W_hat columns bit for bit; zero X
-    gives +0; scaling X by 4 scales Y by 4 exactly; three runs agree bit for
-    bit."""
-    _, w = random_problem(91, 1, 300, 256)
-    q, s = O.quantize(w)
-    x = np.zeros((16, 256), dtype=np.uint16)
-    x[np.arange(16), 17 * np.arange(16)] = 0x3F80                 # bf16 1.0
-    say("stream one-hot")
-    y = run_linear(x, q, s, F.PATH_STREAM)
-    assert np.array_equal(y, O.dequant(q, s)[:, 17 * np.arange(16)].T)
-    say("stream zero input")
-    assert np.all(run_linear(np.zeros((16, 256), np.uint16), q, s, F.PATH_STREAM) == 0)
-    x, w = random_problem(92, 11, 700, 3072)
-    q, s = O.quantize(w)
-    x4 = O.bf16_rne_bits(O.bf16_bits_to_f32(x) * np.float32(4.0))
-    say("stream power-of-two scaling and reproducibility")
-    y1 = run_linear(x, q, s, F.PATH_STREAM)
-    assert np.array_equal(O.bf16_rne_bits(O.bf16_bits_to_f32(y1) * np.float32(4.0)),
-                          run_linear(x4, q, s, F.PATH_STREAM))
-    for _ in range(2):
-        assert np.array_equal(run_linear(x, q, s, F.PATH_STREAM), y1)
-
-
-def test_linear_stream_largest_k_sampled():
-    """K = 2^20 on the streaming kernel: 1024 chunks through the general loop."""
-    m, n, k = 16, 256, 1 << 20
-    rng = np.random.default_rng(39)
-    x = O.bf16_rne_bits(rng.standard_normal((m, k), dtype=np.float32)) & np.uint16(0xFFFF)
-    w = (rng.standard_normal((n, k), dtype=np.float32) * 0.02).astype(np.float32)
-    q, s = O.quantize(w)
-    say("largest K stream", m, n, k)
-    y = run_linear(x, q, s, F.PATH_STREAM)
-    ms = np.array([0, 7, 15]); ns = np.array([0, 255, 128, 3, 31, 32])
-    mm, nn = np.meshgrid(ms, ns, indexing="ij")
-    yr, ar = O.linear_sampled(x, q, s, mm.ravel(), nn.ravel())
-    assert_bound(y[mm.ravel(), nn.ravel()], yr, ar, "largest K stream")
 
 
 @pytest.mark.parametrize("path", ["tiled", "skinny", "large"])
