@@ -8,34 +8,38 @@
 // rows: 2 x 8 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per
 // lane. The decoded weight is the MFMA A operand and X the B operand, so a
 // lane's accumulators hold four consecutive output columns of one output
-// row (8-byte stores). Per 64-wide K step a wave reads 32 X fragments from
+// row (the epilogue regroups them through LDS into whole-line stores). Per 64-wide K step a wave reads 32 X fragments from
 // LDS, and each fragment feeds both of its weight blocks: half the LDS
 // traffic per MFMA of a one-block-per-wave layout. Every code is decoded
 // once per workgroup, by the wave that owns its row.
 //
-// Data movement per step:
+// Data movement per step, through a ring of three LDS stages:
 //  - X: 32 KB per stage, moved global -> LDS by 16-byte buffer loads that
-//    write LDS directly (no registers), into a ring of three stages. The
-//    loads of step k+3 go out right after the barrier of step k, about two
-//    steps ahead of use. The 16-byte chunks of a 128-byte LDS row are
-//    XOR-permuted by (row / 2) % 8, chosen on the global side, so that the
-//    MFMA operand reads (16 lanes on 16 consecutive rows, one chunk) hit 16
-//    distinct bank groups.
-//  - codes: 16 KB per stage, moved global -> LDS the same way into the same
-//    ring (each wave loads only the 64 rows it decodes, 16 rows x 64 bytes
-//    per instruction), the 16-byte chunks of a row XOR-permuted by
-//    (row / 4) % 4 so the decoding reads are conflict-free.
-//  - weight scale: one per wave and step (the wave's 64 rows lie in one
-//    128-row scale block, the 64-wide step in one 128-wide block).
+//    write LDS directly (no registers). The 16-byte chunks of a 128-byte LDS
+//    row are XOR-permuted by (row / 2) % 8, chosen on the global side, so
+//    that the MFMA operand reads (16 lanes on 16 consecutive rows, one
+//    chunk) hit 16 distinct bank groups.
+//  - codes: 16 KB per stage, moved the same way (each wave loads only the 64
+//    rows it decodes, 16 rows x 64 bytes per instruction), the 16-byte
+//    chunks of a row XOR-permuted by (row / 4) % 4 so the decoding reads are
+//    conflict-free.
+//  - weight scale: one word per wave and step, moved into the stage the
+//    same way, so that no global load in the main loop writes a register and
+//    the compiler adds no waits of its own on them.
+//  - the 13 loads of a wave's share of a stage go out two steps ahead,
+//    spread over the first three quarters of a step (one per four MFMAs).
+//    Issued in one burst after the barrier, as four waves at once, they
+//    filled the CU's load queue and held the MFMA stream behind it.
 //
-// Software pipeline inside a step (four sub-steps of k16): while the 16
-// MFMAs of sub-step t run, the wave decodes the codes of sub-step t+1 (32
-// VALU: E4M3 -> fp32 convert, one fp32 multiply by the scale, RNE to bf16)
-// and reads the X fragments of sub-step t+1 from LDS. The decode of the
-// next step's first sub-step runs inside the current step's last one, so
-// the matrix core is never left waiting for VALU work. One barrier per step
-// (inside the last sub-step, after this stage's last operand reads and with
-// the next stage's loads complete).
+// Register pipeline inside a step (four sub-steps of k16, 64 MFMAs): X
+// fragments are read from LDS four ahead of their MFMAs into a ring of
+// eight registers; sub-step t+1's weight operands are decoded during
+// sub-step t (E4M3 -> fp32 convert, one fp32 multiply by the scale, RNE to
+// bf16), the next step's first ones during the last two quarter-sub-steps.
+// The step runs as 16 regions of 4 MFMAs, each with its own share of the
+// reads, the decode and the loads, in a fixed order (a scheduling barrier
+// between regions keeps the compiler from pairing an MFMA with a read it
+// has just issued). One barrier per step, 8 MFMAs before its end.
 //
 // The K order inside a step is a permutation (A and B only have to agree):
 // lane half h holds, for sub-step t, k = 16h + 32(t/2) + 8(t%2) .. +8, so a
@@ -45,8 +49,12 @@
 // descriptors that cover only valid rows and through per-lane out-of-range
 // offsets; no branch in the main loop depends on data.
 //
-// Split-K (gridDim.y > 1): every split writes its fp32 partial tile to the
-// workspace and the ordered reduce kernel adds the splits and rounds once.
+// Persistent: one workgroup per CU walks its (tile, K split) units; the
+// loads of the next unit's first two steps go out during the last two steps
+// of the current one, so the ring never drains between units.
+//
+// Split-K (units with a K split): every split writes its fp32 partial tile to
+// the workspace and the ordered reduce kernel adds the splits and rounds once.
 #include <atomic>
 
 #include "fp8bl_device.h"
@@ -64,7 +72,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 3;
 constexpr int kXElems = kBM * kBK;          // bf16 elements of one stage's X tile (32 KB)
 constexpr int kWBytes = kBN * kBK;          // bytes of one stage's codes (16 KB)
-constexpr int kStageElems = kXElems + kWBytes / 2;   // stage size in bf16 elements (48 KB)
+constexpr int kSElems = kWaves * 64 * 4 / 2;  // the waves' block-scale slots (256 B each)
+constexpr int kStageElems = kXElems + kWBytes / 2 + kSElems;   // stage size in bf16 elements (49 KB)
 constexpr int kXLoads = kXElems * 2 / 16 / kThreads;   // 16-byte X loads per lane per step
 constexpr int kWLoads = kWBytes / 16 / kThreads;       // 16-byte code loads per lane per step
 constexpr int kLoadsPerStep = kXLoads + kWLoads + 1;   // + the scale
@@ -73,6 +82,8 @@ constexpr uint32_t kOob = 0x80000000u;      // buffer offset past every valid ra
 static_assert(kXLoads == 8, "one wave's X loads cover 64 rows of a stage");
 static_assert(kWLoads == 4, "one wave's code loads cover its 64 rows of a stage");
 static_assert(kBK == 64, "the X chunk permutation assumes 128-byte LDS rows");
+static_assert(kLoadsPerStep == 13, "the load slots of the step schedule assume 13 loads");
+static_assert((kStageElems * 2) % 256 == 0, "stages keep the LDS bank phase of their rows");
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14],
 // expcnt[6:4], lgkmcnt[11:8]). vm_wait(n): at most n vector-memory
@@ -160,8 +171,8 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(s, (uint32_t)(((N + kBlock - 1) / kBlock) * gk * 4));
 
-  // The unit whose steps are being loaded (up to three steps ahead of the
-  // one being computed, so at the end of a unit it is the next one).
+  // The unit whose steps are being loaded (two steps ahead of the one being
+  // computed, so near the end of a unit it is the next one).
   Unit LU = unit_of(0);
   __amdgpu_buffer_rsrc_t xrs, wrs;
   bool lwave_live;
@@ -175,40 +186,49 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   };
   set_load_unit(LU);
 
-  auto issue_x = [&](int stage, int kt) {
+  // Stage loads. `sb` is the stage's first element in xs (wave-uniform).
+  // X load i (of 8) and code load i (of 4) as above; each sends a 1 KB
+  // wave-wide piece straight into LDS.
+  auto issue_x = [&](int sb, int kt, int i) {
     const int kbase = (LU.kt0 + kt) * kBK;
     // K left in this step (0 past the unit's range): a chunk is read iff it
     // starts below it
     const int klim = kt < LU.nreal ? K - kbase : 0;
-    const uint32_t soff = (uint32_t)(kbase * 2);
-    const bool in_even = xc_even * 8 < klim, in_odd = xc_odd * 8 < klim;
-#pragma unroll
-    for (int i = 0; i < kXLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (lds_ptr_t)&xs[stage * kStageElems + (64 * wave + 8 * i) * kBK], 16,
-          ((i & 1) ? in_odd : in_even) ? xvo[i] : kOob, soff, 0, 0);
+    const bool in = ((i & 1) ? xc_odd : xc_even) * 8 < klim;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr_t)&xs[sb + (64 * wave + 8 * i) * kBK], 16,
+                                             in ? xvo[i] : kOob, (uint32_t)(kbase * 2), 0, 0);
   };
-  auto issue_w = [&](int stage, int kt) {
+  auto issue_w = [&](int sb, int kt, int i) {
     const int kbase = (LU.kt0 + kt) * kBK;
     const int klim = kt < LU.nreal ? K - kbase : 0;
     const bool kin = 16 * wc < klim;
-#pragma unroll
-    for (int i = 0; i < kWLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wrs, (lds_ptr_t)&xs[stage * kStageElems + kXElems + (64 * wave + 16 * i) * kBK / 2], 16,
-          kin ? wvo[i] : kOob, (uint32_t)kbase, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wrs, (lds_ptr_t)&xs[sb + kXElems + (64 * wave + 16 * i) * kBK / 2], 16,
+        kin ? wvo[i] : kOob, (uint32_t)kbase, 0, 0);
   };
-  // Weight scale: one per wave and step, loaded with the step's codes as a
-  // vector load (every lane the same address), so it rides the same counter
-  // as the codes and no scalar load is ever in flight next to the operand
-  // reads. Waves past N and dead steps read zero. (The address is always
-  // formed, block clamped, and pushed out of range when dead: a select
-  // between two computed offsets became a branch.)
-  auto issue_s = [&](float& sc, int kt) {
+  // Weight scale: one per wave and step (the wave's 64 rows lie in one
+  // 128-row scale block, the 64-wide step in one 128-wide block), moved into
+  // the stage like the codes: every lane fetches the same word, so the
+  // wave's 256-byte slot holds 64 copies. No load in the main loop writes a
+  // register, so the only waits on global loads are the explicit ones below.
+  // Waves past N and dead steps read zero. (The address is always formed,
+  // block clamped, and pushed out of range when dead.)
+  auto issue_s = [&](int sb, int kt) {
     const int kb = min(((LU.kt0 + kt) * kBK) / kBlock, gk - 1);
     const bool live = lwave_live & (kt < LU.nreal);
     const uint32_t off = (uint32_t)((lsrow * gk + kb) * 4) + (live ? 0u : kOob);
-    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        srs, (lds_ptr_t)&xs[sb + kXElems + kWBytes / 2 + wave * 128], 4, off, 0, 0, 0);
+  };
+  auto issue_all = [&](int sb, int kt) {
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) issue_x(sb, kt, i);
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) issue_w(sb, kt, i);
+    issue_s(sb, kt);
+  };
+  auto read_s = [&](int sb) -> float {
+    return *reinterpret_cast<const float*>(&xs[sb + kXElems + kWBytes / 2 + wave * 128]);
   };
 
   // Codes of weight block nb, K half j of a stage (the 16 codes of sub-steps
@@ -218,26 +238,20 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   const int cswz = ((lane & 31) >> 2) & 3;
   const int crd0 = crow + ((((lane >> 5) + 0) ^ cswz) << 4);
   const int crd1 = crow + ((((lane >> 5) + 2) ^ cswz) << 4);
-  auto read_w = [&](u32x4 (&c)[2], int stage, int j) {
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(&xs[stage * kStageElems + kXElems]) + (j ? crd1 : crd0);
+  auto read_w = [&](u32x4 (&c)[2], int sb, int j) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(&xs[sb + kXElems]) + (j ? crd1 : crd0);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) c[nb] = *reinterpret_cast<const u32x4*>(base + nb * 32 * kBK);
   };
-  // Sub-step t from the codes of its K half -> the two A operands.
-  auto decode = [&](bf16x8 (&wd)[2], const u32x4 (&c)[2], float sc, int t) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) wd[nb] = dequant8(c[nb][(t & 1) * 2], c[nb][(t & 1) * 2 + 1], sc);
-  };
-  // Sub-step t of a stage -> the eight B operands (X row blocks 0..7).
+  // X fragment f of a stage (sub-step t = f / 8, row block mb = f % 8): the
+  // MFMA B operand of the 32 X rows 32mb.. and the 16 K of sub-step t.
   const int arow = lane & 31;
   const int ahalf = lane >> 5;
   const int aswz = (arow >> 1) & 7;
-  auto read_x = [&](bf16x8 (&xf)[8], int stage, int t) {
+  auto read_xf = [&](int sb, int f) -> bf16x8 {
+    const int t = f >> 3, mb = f & 7;
     const int c = 2 * ahalf + 4 * (t >> 1) + (t & 1);
-    const uint16_t* base = &xs[stage * kStageElems + arow * kBK + ((c ^ aswz) << 3)];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      xf[mb] = *reinterpret_cast<const bf16x8*>(base + mb * 32 * kBK);
+    return *reinterpret_cast<const bf16x8*>(&xs[sb + arow * kBK + ((c ^ aswz) << 3) + mb * 32 * kBK]);
   };
 
   f32x16 acc[2][8];
@@ -248,124 +262,136 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
 
-  // MFMAs of blocks [mb_lo, mb_hi) for one sub-step.
-  auto mfma_part = [&](const bf16x8 (&wd)[2], const bf16x8 (&xf)[8], int mb_lo, int mb_hi) {
-#pragma unroll
-    for (int mb = mb_lo; mb < mb_hi; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wd[nb], xf[mb], acc[nb][mb], 0, 0, 0);
-  };
-
-  float ss0, ss1, ss2;
-  u32x4 cA[2], cB[2];      // codes of K halves 0 and 1 of a step
-  bf16x8 wd0[2], wd1[2];
-  bf16x8 xf0[8], xf1[8];
-
-  // Prologue: steps 0, 1, 2 of the first unit in flight (every unit has a
-  // multiple of three steps); wait for step 0, then prepare the first
-  // sub-step's operands.
-  issue_x(0, 0);
-  issue_w(0, 0);
-  issue_s(ss0, 0);
-  issue_x(1, 1);
-  issue_w(1, 1);
-  issue_s(ss1, 1);
-  issue_x(2, 2);
-  issue_w(2, 2);
-  issue_s(ss2, 2);
-  __builtin_amdgcn_s_waitcnt(vm_wait(2 * kLoadsPerStep));
-  __builtin_amdgcn_s_barrier();
-  read_w(cA, 0, 0);
-  decode(wd0, cA, ss0, 0);
-  read_x(xf0, 0, 0);
-
-  // One sub-step's MFMAs with the next sub-step's decode and operand reads
-  // spread between them.
-  auto interleave16 = [&]() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-
-  // One step: scale of this step in sc, of the next in scn; X and codes in
-  // stage S; `lkt` is the step of the load unit to fetch into the stage this
-  // step frees and into sc. On entry wd0/xf0 hold sub-step 0's operands and
-  // cA the codes of K half 0; on exit, the same for the next step.
-  auto step = [&](int S, int lkt, float& sc, float& scn) {
-    const int Sn = S == kStages - 1 ? 0 : S + 1;
-    // sub-step 0: MFMAs on (wd0, xf0); prepare sub-step 1 into (wd1, xf1)
-    // and read the codes of K half 1
-    decode(wd1, cA, sc, 1);
-    read_x(xf1, S, 1);
-    read_w(cB, S, 1);
-    mfma_part(wd0, xf0, 0, 8);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      if (i < 10) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // sub-step 1
-    decode(wd0, cB, sc, 2);
-    read_x(xf0, S, 2);
-    mfma_part(wd1, xf1, 0, 8);
-    interleave16();
-    __builtin_amdgcn_sched_barrier(0);
-    // sub-step 2
-    decode(wd1, cB, sc, 3);
-    read_x(xf1, S, 3);
-    mfma_part(wd0, xf0, 0, 8);
-    interleave16();
-    __builtin_amdgcn_sched_barrier(0);
-    // sub-step 3, first half: its operands are in registers once this
-    // wave's reads of stage S have returned.
-    __builtin_amdgcn_s_waitcnt(kLgkmWait0);
-    mfma_part(wd1, xf1, 0, 4);
-    __builtin_amdgcn_sched_barrier(0);
-    // The next step's loads have landed (only the step after it may still be
-    // in flight), and every wave is done reading stage S: refill it three
-    // steps ahead and reuse this step's scale register for that step. The
-    // loads, the next step's first code reads, decode and operand reads run
-    // between the second half's MFMAs.
-    __builtin_amdgcn_s_waitcnt(vm_wait(kLoadsPerStep));
+  // Workgroup barrier; the empty asm statements keep the compiler from
+  // moving any memory access (LDS reads included) across it.
+  auto wg_barrier = [] {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_x(S, lkt);
-    issue_w(S, lkt);
-    issue_s(sc, lkt);
-    read_w(cA, Sn, 0);
-    decode(wd0, cA, scn, 0);
-    read_x(xf0, Sn, 0);
-    mfma_part(wd1, xf1, 4, 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
   };
+
+  // ---- Register pipeline of a step (32 fragments f = 8t + mb; sub-step t
+  // runs the 16 MFMAs of its 8 X fragments against its two decoded weight
+  // operands):
+  //  - X fragments are read four ahead of their MFMAs into a ring of eight;
+  //    the last four of a step read the next stage, after the barrier;
+  //  - sub-step t+1's weight operands are decoded during sub-step t (the
+  //    next step's first ones during sub-step 3), codes read a K half ahead;
+  //  - the 13 loads of the step two ahead are spread over fragments 0..24;
+  //  - at fragment 24 the wave waits for its loads of the next step (the
+  //    ones issued during the previous step) and reads its codes and scale;
+  //  - at fragment 28 the barrier: every wave is done with this stage (its
+  //    last reads returned), and the next stage is complete.
+  // fragments f..f+5 are live in the region of f, f+1; 8 slots keep the
+  // slot of a fragment the same in every step (32 fragments a step)
+  constexpr int kRing = 8;
+  constexpr int kAhead = 4;
+  bf16x8 xr[kRing];
+  u32x4 wdh[2][2];          // decoded weight operands (bf16 pairs), by sub-step parity
+  u32x4 cA[2], cB[2];       // codes of K halves 0 and 1
+  float sc;                 // this step's scale
+
+  // Prologue: steps 0 and 1 of the first unit in flight (every unit has at
+  // least three steps); wait for step 0, then prepare its first operands.
+  issue_all(0, 0);
+  issue_all(kStageElems, 1);
+  __builtin_amdgcn_s_waitcnt(vm_wait(kLoadsPerStep));
+  wg_barrier();
+  read_w(cA, 0, 0);
+  sc = read_s(0);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) wdh[0][nb] = __builtin_bit_cast(u32x4, dequant8(cA[nb][0], cA[nb][1], sc));
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) xr[f] = read_xf(0, f);
 
   const int col_lane = 64 * wave + 4 * ahalf;
+  int S = 0;                 // stage of the step being computed
+  int lkt = 1;               // step (of LU) most recently loaded
   for (int ci = 0; ci < my_units; ++ci) {
-    for (int kt = 0; kt < steps_per_unit; kt += 3) {
-      // The loads of this triple are steps kt+3..kt+5 of this unit, or,
-      // for its last triple, steps 0..2 of the next.
-      int lkt = kt + 3;
-      if (lkt == steps_per_unit) {
-        set_load_unit(unit_of(ci + 1));
-        lkt = 0;
-      }
-      step(0, lkt, ss0, ss1);
-      step(1, lkt + 1, ss1, ss2);
-      step(2, lkt + 2, ss2, ss0);
+  for (int kt = 0; kt < steps_per_unit; ++kt) {
+    // the step two ahead: next step of LU, or step 0 of the next unit
+    if (++lkt == steps_per_unit) {
+      set_load_unit(unit_of(ci + 1));
+      lkt = 0;
     }
+    const int Sn = S == kStages - 1 ? 0 : S + 1;
+    const int L = Sn == kStages - 1 ? 0 : Sn + 1;
+    const int sb = S * kStageElems, sbn = Sn * kStageElems, sbl = L * kStageElems;
+
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t == 0) read_w(cB, sb, 1);
+#pragma unroll
+      for (int mb = 0; mb < 8; mb += 2) {
+        // one region: the MFMAs of fragments f, f+1 with their share of the
+        // other work, in a fixed order relative to the other regions
+        const int f = 8 * t + mb;
+        if (f == 24) {
+          // this wave's loads of the next step (issued during the previous
+          // step) have landed, with 12 of this step's still in flight: read
+          // its codes of K half 0 and its scale
+          __builtin_amdgcn_s_waitcnt(vm_wait(kLoadsPerStep - 1));
+          read_w(cA, sbn, 0);
+          sc = read_s(sbn);
+        }
+        if (f == 28) {
+          // every wave is done with this stage (its last reads returned)
+          // and has put its part of the next stage in place
+          __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+          wg_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // read ahead (the last four from the next stage, after the barrier)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int fa = f + j + kAhead;
+          xr[fa % kRing] = fa < 32 ? read_xf(sb, fa) : read_xf(sbn, fa - 32);
+        }
+        // the loads of the step two ahead, into the stage freed by the last barrier
+        if (f <= 14) issue_x(sbl, lkt, (f >> 1) + 0);
+        if (f >= 16 && f <= 22) issue_w(sbl, lkt, (f - 16) >> 1);
+        if (f == 24) issue_s(sbl, lkt);
+        // the next sub-step's weight operands, a quarter (one block's half
+        // K of the sub-step: four codes to bf16) per region: sub-steps 1..3
+        // from this step's codes, the next step's sub-step 0 from its codes
+        // read at fragment 24, in the two regions after the barrier
+        auto piece = [&](int q4) {
+          const int nb = q4 >> 1, half = q4 & 1;
+          const int tn = (t + 1) & 3;          // sub-step being prepared
+          const u32x4 (&c)[2] = tn <= 1 ? cA : cB;
+          const u32x2 v = dequant4(c[nb][2 * (tn & 1) + half], sc);
+          wdh[tn & 1][nb][2 * half] = v[0];
+          wdh[tn & 1][nb][2 * half + 1] = v[1];
+        };
+        if (t < 3) {
+          piece(mb >> 1);
+        } else if (f >= 28) {
+          piece(f - 28);
+          piece(f - 28 + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[nb][mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, wdh[t & 1][nb]), xr[(f + j) % kRing], acc[nb][mb + j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    S = Sn;
+  }
 
     // ---- Epilogue of unit ci (the next unit's first loads are already in
     // flight). acc[nb][mb][4g + e] is output row m0 + 32mb + l%32, column
@@ -379,19 +405,64 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     if constexpr (!SPLIT) {
       const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + (size_t)CU.m0 * N, (uint32_t)(rows * N * 2));
       if ((N & 3) == 0) {
+        if ((N & 7) == 0) {
+          // Through LDS, so that every store writes whole 128-byte lines:
+          // lane l holds four consecutive columns of row l % 32 of each
+          // 32x32 block, so direct stores write 16 bytes into each of 32
+          // rows, and eight of them fill a line; written to memory that way
+          // a tile takes about three times as long. Each 32-row block of
+          // this wave's 256 x 64 slice goes row-major into 4 KB of LDS (16-byte
+          // chunk c of row r at chunk c ^ ((r / 2) % 8)), then comes back as
+          // 16 bytes per lane, 8 lanes per 128-byte row, 8 rows per store.
+          // The LDS is the wave's own 8 KB of X rows in the stage the last
+          // step used: every wave finished reading that stage before the last
+          // barrier, and only this wave refills those rows, with loads it
+          // issues after these reads have returned.
+          const int tb = (S == 0 ? 2 : S - 1) * kStageElems + wave * 64 * kBK;
+          // (the lane index through an empty asm: the compiler would otherwise
+          // compute every address below once, before the loops, and keep
+          // them in registers the main loop needs)
+          int le;
+          asm volatile("" : "=v"(le) : "0"(lane));
+          const int er = le & 31, eh = le >> 5;
+          const int rr = le >> 3;                   // row within 8 for the read-back
+          const int col8 = CU.n0 + 64 * wave + 8 * (le & 7);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+          for (int mb = 0; mb < 8; ++mb) {
+            uint16_t* buf = &xs[tb + (mb & 1) * 2048];
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int col = col_base + 32 * nb + 8 * g;
-              const uint32_t off = col < N ? (uint32_t)(((arow + 32 * mb) * N + col) * 2) : kOob;
-              const f32x16& a = acc[nb][mb];
-              const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
-              __builtin_amdgcn_raw_buffer_store_b64(v, yrs, off, 0, 0);
-              __builtin_amdgcn_sched_barrier(0);
+              for (int g = 0; g < 4; ++g) {
+                const f32x16& a = acc[nb][mb];
+                const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+                const int chunk = (4 * nb + g) ^ ((er >> 1) & 7);
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(buf) + er * 128 + chunk * 16 + 8 * eh) = v;
+              }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 8 * j + rr;
+              const u32x4 v = *reinterpret_cast<const u32x4*>(
+                  reinterpret_cast<const uint8_t*>(buf) + r * 128 + (((le & 7) ^ ((r >> 1) & 7)) * 16));
+              const uint32_t off = col8 < N ? (uint32_t)(((32 * mb + r) * N + col8) * 2) : kOob;
+              __builtin_amdgcn_raw_buffer_store_b128(v, yrs, off, 0, 0);
             }
+          }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int col = col_base + 32 * nb + 8 * g;
+                const uint32_t off = col < N ? (uint32_t)(((arow + 32 * mb) * N + col) * 2) : kOob;
+                const f32x16& a = acc[nb][mb];
+                const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+                __builtin_amdgcn_raw_buffer_store_b64(v, yrs, off, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+        }
       } else {
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
@@ -502,10 +573,10 @@ hipError_t launch_gemm_large(const uint16_t* x, const uint8_t* q, const float* s
   const int tiles_m = (int)((m + kBM - 1) / kBM);
   const int tiles_n = (int)((n + kBN - 1) / kBN);
   const int units = tiles_m * tiles_n * p.splits;
-  // one persistent workgroup per CU; every unit padded to a multiple of
-  // three steps (the register ring's period; padded steps read zeros)
+  // one persistent workgroup per CU; every unit has at least two steps (the
+  // prologue loads two; a padded step reads zeros)
   const int grid = units < device_cus() ? units : device_cus();
-  const int spu = (p.kt_per_split + 2) / 3 * 3;
+  const int spu = p.kt_per_split > 2 ? p.kt_per_split : 2;
   if (p.splits == 1) {
     hipLaunchKernelGGL(gemm_large_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
                        x, q, s, y, nullptr, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,

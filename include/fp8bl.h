@@ -56,11 +56,12 @@ enum fp8bl_status {
   FP8BL_HIP_ERROR = 5           /* a HIP runtime call failed (device query or launch) */
 };
 
-/* Kernel choice for fp8_block_linear_ex. AUTO picks SKINNY for M <= 32 and
- * one of the two tiled kernels otherwise; the other values force a kernel
- * (for tests and measurements). TILED is the tile-planned kernel (128- and
- * 256-row tiles), LARGE the 256x256 four-wave kernel, which takes shapes
- * with N < 2^21 (FP8BL_INVALID_ARG otherwise). */
+/* Kernel choice for fp8_block_linear_ex. AUTO picks SKINNY for M <= 32,
+ * LARGE when the shape has at least 512 of its 256x256 tiles (and N < 2^21),
+ * TILED otherwise; the other values force a kernel (for tests and
+ * measurements). TILED is the tile-planned kernel (128- and 256-row tiles),
+ * LARGE the 256x256 four-wave kernel, which takes shapes with N < 2^21
+ * (FP8BL_INVALID_ARG otherwise). */
 enum fp8bl_path {
   FP8BL_PATH_AUTO = 0,
   FP8BL_PATH_TILED = 1,
