@@ -173,17 +173,17 @@ FP8BL_EXPORT size_t fp8_block_linear_workspace_size(int64_t m, int64_t n, int64_
 namespace {
 
 // The kernel a call runs: the forced one, or the library's choice for AUTO:
-// the weight-streaming kernel up to 32 rows, the 256x256 four-wave kernel
-// once the shape has at least two of its tiles per compute unit (measured on
-// MI355X: 12-15% faster than the tile-planned kernel at 16384 x 3072 x 3072
-// and 16384 x 12288 x 3072, slower where its tiles leave CUs idle), else
-// the tile-planned kernel.
+// the weight-streaming kernel up to 32 rows, otherwise whichever of the two
+// fused kernels the planners' cost models (same units, fitted to MI355X
+// measurements) expect to finish first. The 256x256 persistent kernel wins
+// on large shapes (16384 x 12288 x 3072: 945 against 1062 us) and on 512-row
+// shapes whose units fill the CUs once (512 x 25600 x 5120: 131 against 158
+// us; 512 x 5120 x 25600 with 6 K splits: 126 against 143 us).
 int resolve_path(int path, int64_t m, int64_t n, int64_t k) {
-  (void)k;
   if (path != FP8BL_PATH_AUTO) return path;
   if (m <= kSkinnyMaxM) return FP8BL_PATH_SKINNY;
-  const int64_t large_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (n < kLargeMaxN && large_tiles >= 512) return FP8BL_PATH_LARGE;
+  if (n < kLargeMaxN && fp8bl::plan_large(m, n, k).cost < fp8bl::tiled_cost(m, n, k))
+    return FP8BL_PATH_LARGE;
   return FP8BL_PATH_TILED;
 }
 

@@ -25,8 +25,10 @@ hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q
                             uint16_t* y, int64_t m, int64_t n, int64_t k, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
-// Large-M fused GEMM (E4M3 tiles decoded to bf16 in registers, bf16 MFMA).
+// Tile-planned fused GEMM (E4M3 tiles decoded to bf16 in registers, bf16
+// MFMA); tiled_cost is its planner's time estimate for the chosen plan.
 size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k);
+double tiled_cost(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s,
                              uint16_t* y, int64_t m, int64_t n, int64_t k,
                              void* ws, size_t ws_bytes, hipStream_t stream);
@@ -35,6 +37,7 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
 // direct-to-LDS ring, codes decoded one sub-step ahead of the MFMAs.
 struct LargePlan {
   int splits, kt_per_split;
+  double cost;      // planner's time estimate, the units of tiled_cost
 };
 LargePlan plan_large(int64_t m, int64_t n, int64_t k);
 size_t large_workspace_bytes(int64_t m, int64_t n, int64_t k);

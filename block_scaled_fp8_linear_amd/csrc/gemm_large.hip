@@ -482,22 +482,39 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
           make_rsrc(part + (size_t)CU.split * partial_slab(M, N) + (size_t)CU.m0 * N,
                     (uint32_t)(rows * N * 4));
       if ((N & 3) == 0) {
+        // fp32 partials through the same LDS slice, as whole lines: each
+        // 32-row block of this wave's 256 x 64 slice row-major in its 8 KB
+        // (256-byte rows, 16-byte chunk c of row r at c ^ (r % 16)), back as
+        // 16 bytes per lane, 16 lanes per row, 4 rows per store.
+        const int tb = (S == 0 ? 2 : S - 1) * kStageElems + wave * 64 * kBK;
+        int le;
+        asm volatile("" : "=v"(le) : "0"(lane));
+        const int er = le & 31, eh = le >> 5;
+        const int cc = le & 15, rq = le >> 4;
+        const int col4 = CU.n0 + 64 * wave + 4 * cc;
+        uint8_t* buf = reinterpret_cast<uint8_t*>(&xs[tb]);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+        for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int col = col_base + 32 * nb + 8 * g;
-              const uint32_t off = col < N ? (uint32_t)(((arow + 32 * mb) * N + col) * 4) : kOob;
               const f32x16& a = acc[nb][mb];
               // (__builtin_bit_cast of a vector element read element 0 here:
               // the values go through __float_as_uint instead.)
               const u32x4 v = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
                                __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
-              __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, 0);
-              __builtin_amdgcn_sched_barrier(0);
+              const int c = 8 * nb + 2 * g + eh;
+              *reinterpret_cast<u32x4*>(buf + er * 256 + ((c ^ (er & 15)) << 4)) = v;
             }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 4 * j + rq;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(buf + r * 256 + ((cc ^ (r & 15)) << 4));
+            const uint32_t off = col4 < N ? (uint32_t)(((32 * mb + r) * N + col4) * 4) : kOob;
+            __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, 0);
+          }
+        }
       } else {
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
@@ -526,16 +543,33 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 
 }  // namespace
 
+// Split count from the cost model of the tile-planned kernel's planner, in
+// the same units (microseconds, work counted in 128x128x64 steps): a CU
+// runs this kernel's 256x256x64 step (4 of those) at 2.42 of them per
+// microsecond (measured on 16384 x 12288 x 3072), plus about 2 us per unit
+// for its first loads and its epilogue; the busiest CU sets the time, ceil(units /
+// 256) units. K splits add the fp32 partials' round trip (as in that
+// planner). The split count that puts about one unit on every CU wins at
+// 512 rows (e.g. 6 for 512 x 5120 x 25600).
 LargePlan plan_large(int64_t m, int64_t n, int64_t k) {
   const int nkt = (int)((k + kBK - 1) / kBK);
   const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
-  int splits = 1;
-  // Split K only while the tiles leave most CUs idle and each split keeps
-  // at least 8 steps.
-  while (tiles * splits * 2 <= 256 && (nkt + 2 * splits - 1) / (2 * splits) >= 8) splits *= 2;
-  LargePlan p;
-  p.kt_per_split = (nkt + splits - 1) / splits;
+  LargePlan p{1, nkt, 0.0};
+  double best = 1e300;
+  for (int sp = 1; sp <= 8; ++sp) {
+    const int steps = (nkt + sp - 1) / sp;
+    if (sp > 1 && steps < 8) break;
+    const int64_t per_cu = (tiles * sp + 255) / 256;
+    double cost = (double)per_cu * (steps * 4 / 2.42 + 2.0);
+    if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
+    if (cost < best) {
+      best = cost;
+      p.splits = sp;
+    }
+  }
+  p.kt_per_split = (nkt + p.splits - 1) / p.splits;
   p.splits = (nkt + p.kt_per_split - 1) / p.kt_per_split;
+  p.cost = best;
   return p;
 }
 

@@ -474,7 +474,7 @@ double cu_rate(int cfg, int64_t per_cu) {
   return per_cu <= 1 ? 1.44 : 1.90;
 }
 
-TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
+TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, double* cost_out = nullptr) {
   const int nkt = (int)((k + kBK - 1) / kBK);
   // evaluation order breaks ties: 256x128 first below 2048 rows
   const int order_small[4] = {1, 0, 2, 3}, order_large[4] = {3, 0, 1, 2};
@@ -500,10 +500,17 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k) {
   }
   best.kt_per_split = best.splits > 1 ? (nkt + best.splits - 1) / best.splits : nkt;
   best.splits = (nkt + best.kt_per_split - 1) / best.kt_per_split;
+  if (cost_out) *cost_out = best_cost;
   return best;
 }
 
 }  // namespace
+
+double tiled_cost(int64_t m, int64_t n, int64_t k) {
+  double c = 0.0;
+  (void)plan_tiled(m, n, k, &c);
+  return c;
+}
 
 // Workspace: the fp32 partials of every split.
 size_t tiled_workspace_bytes(int64_t m, int64_t n, int64_t k) {
