@@ -56,12 +56,14 @@ enum fp8bl_status {
   FP8BL_HIP_ERROR = 5           /* a HIP runtime call failed (device query or launch) */
 };
 
-/* Kernel choice for fp8_block_linear_ex. AUTO picks SKINNY for M <= 32,
- * LARGE when the shape has at least 512 of its 256x256 tiles (and N < 2^21),
- * TILED otherwise; the other values force a kernel (for tests and
- * measurements). TILED is the tile-planned kernel (128- and 256-row tiles),
- * LARGE the 256x256 four-wave kernel, which takes shapes with N < 2^21
- * (FP8BL_INVALID_ARG otherwise). */
+/* Kernel choice for fp8_block_linear_ex. AUTO picks SKINNY for M <= 32 and
+ * otherwise whichever of TILED and LARGE the library's cost model expects to
+ * be faster for the shape (LARGE only for N < 2^21); the other values force
+ * a kernel (for tests and measurements). TILED is the tile-planned kernel
+ * (128- and 256-row tiles), LARGE the persistent 256x256 four-wave kernel,
+ * which takes shapes with N < 2^21 (FP8BL_INVALID_ARG otherwise). Every
+ * kernel computes the same function to the same error bound; results may
+ * differ in the last bits between kernels (different K split counts). */
 enum fp8bl_path {
   FP8BL_PATH_AUTO = 0,
   FP8BL_PATH_TILED = 1,
