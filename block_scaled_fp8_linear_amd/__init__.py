@@ -174,9 +174,10 @@ def fp8_block_linear_noalloc(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
 
 def fp8_block_mlp_gate_up(x: torch.Tensor, q_gate: torch.Tensor, s_gate: torch.Tensor,
                           q_up: torch.Tensor, s_up: torch.Tensor,
-                          out: torch.Tensor | None = None) -> torch.Tensor:
+                          out: torch.Tensor | None = None, path: int = PATH_AUTO) -> torch.Tensor:
     """bf16 x [M,K] and two block-FP8 weights [N,K] -> bf16 h [M,N] with
-    h = bf16(bf16(silu(g)) * u), g and u the two linears' bf16 outputs."""
+    h = bf16(bf16(silu(g)) * u), g and u the two linears' bf16 outputs.
+    ``path``: PATH_AUTO, PATH_TILED or PATH_LARGE (N % 8 == 0)."""
     _need(x, torch.bfloat16, "x")
     for t, name in ((q_gate, "q_gate"), (q_up, "q_up")):
         _need(t, torch.uint8, name)
@@ -195,9 +196,10 @@ def fp8_block_mlp_gate_up(x: torch.Tensor, q_gate: torch.Tensor, s_gate: torch.T
     if tuple(out.shape) != (m, n):
         raise ValueError("out shape")
     with torch.cuda.device(x.device):
-        _check(_lib.mlp_gate_up_raw(x.data_ptr(), q_gate.data_ptr(), s_gate.data_ptr(),
-                                    q_up.data_ptr(), s_up.data_ptr(), out.data_ptr(),
-                                    m, n, k, _stream(x.device)), "fp8_block_mlp_gate_up")
+        _check(_lib.mlp_gate_up_ex_raw(x.data_ptr(), q_gate.data_ptr(), s_gate.data_ptr(),
+                                       q_up.data_ptr(), s_up.data_ptr(), out.data_ptr(),
+                                       m, n, k, int(path), _stream(x.device)),
+               "fp8_block_mlp_gate_up")
     return out
 
 

@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_linear_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_block_mlp_gate_up.restype = c_int
     lib.fp8_block_mlp_gate_up.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_block_mlp_gate_up_ex.restype = c_int
+    lib.fp8_block_mlp_gate_up_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fp8_act_quantize.restype = c_int
     lib.fp8_act_quantize.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fp8_block_linear_w8a8_workspace_size.restype = sz
@@ -128,6 +130,11 @@ NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 def mlp_gate_up_raw(x: int, qg: int, sg: int, qu: int, su: int, h: int,
                     m: int, n: int, k: int, stream: int = 0) -> int:
     return load().fp8_block_mlp_gate_up(x, qg, sg, qu, su, h, m, n, k, stream)
+
+
+def mlp_gate_up_ex_raw(x: int, qg: int, sg: int, qu: int, su: int, h: int,
+                       m: int, n: int, k: int, path: int, stream: int = 0) -> int:
+    return load().fp8_block_mlp_gate_up_ex(x, qg, sg, qu, su, h, m, n, k, path, stream)
 
 
 def act_quantize_raw(x: int, xq: int, xs: int, m: int, k: int, stream: int = 0) -> int:

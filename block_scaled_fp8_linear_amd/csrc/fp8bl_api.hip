@@ -287,10 +287,13 @@ FP8BL_EXPORT int fp8_block_linear(const uint16_t* x, const uint8_t* q, const flo
                              FP8BL_PATH_AUTO, stream);
 }
 
-FP8BL_EXPORT int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate,
-                                       const float* scale_inv_gate, const uint8_t* q_up,
-                                       const float* scale_inv_up, uint16_t* h, int64_t m,
-                                       int64_t n, int64_t k, hipStream_t stream) {
+FP8BL_EXPORT int fp8_block_mlp_gate_up_ex(const uint16_t* x, const uint8_t* q_gate,
+                                          const float* scale_inv_gate, const uint8_t* q_up,
+                                          const float* scale_inv_up, uint16_t* h, int64_t m,
+                                          int64_t n, int64_t k, int path, hipStream_t stream) {
+  if (path != FP8BL_PATH_AUTO && path != FP8BL_PATH_TILED && path != FP8BL_PATH_LARGE)
+    return FP8BL_INVALID_ARG;
+  if (path == FP8BL_PATH_LARGE && (n % 8 != 0 || n >= kLargeMaxN)) return FP8BL_INVALID_ARG;
   int st = validate_linear(x, q_gate, scale_inv_gate, h, m, n, k, FP8BL_PATH_AUTO);
   if (st != FP8BL_OK) return st;
   st = validate_linear(x, q_up, scale_inv_up, h, m, n, k, FP8BL_PATH_AUTO);
@@ -298,8 +301,24 @@ FP8BL_EXPORT int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate,
   if (m == 0 || n == 0) return FP8BL_OK;
   st = gate_current_device();
   if (st != FP8BL_OK) return st;
+  if (path == FP8BL_PATH_AUTO)
+    path = (n % 8 == 0 && n < kLargeMaxN &&
+            fp8bl::large_gated_cost(m, n, k) < fp8bl::mlp_tiled_cost(m, n, k))
+               ? FP8BL_PATH_LARGE
+               : FP8BL_PATH_TILED;
+  if (path == FP8BL_PATH_LARGE)
+    return hip_status(fp8bl::launch_gemm_large_gated(x, q_gate, scale_inv_gate, q_up,
+                                                     scale_inv_up, h, m, n, k, stream));
   return hip_status(fp8bl::launch_mlp_gate_up(x, q_gate, scale_inv_gate, q_up, scale_inv_up, h,
                                               m, n, k, stream));
+}
+
+FP8BL_EXPORT int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate,
+                                       const float* scale_inv_gate, const uint8_t* q_up,
+                                       const float* scale_inv_up, uint16_t* h, int64_t m,
+                                       int64_t n, int64_t k, hipStream_t stream) {
+  return fp8_block_mlp_gate_up_ex(x, q_gate, scale_inv_gate, q_up, scale_inv_up, h, m, n, k,
+                                  FP8BL_PATH_AUTO, stream);
 }
 
 FP8BL_EXPORT int fp8_act_quantize(const uint16_t* x, uint8_t* xq, float* x_scale, int64_t m,

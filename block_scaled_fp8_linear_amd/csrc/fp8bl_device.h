@@ -61,4 +61,33 @@ __device__ __forceinline__ uint32_t canon_nan_bf16x2(uint32_t v) {
   return lo | (hi << 16);
 }
 
+// bf16 SwiGLU of two fp32 accumulators, rounded where eager bf16 ops round
+// (FastVideo fasth3_omniref_b200 README, "What --lossless-accel turns on"):
+// g and u each to bf16, silu(g) = g / (1 + e^-g) in fp32 then to bf16, and
+// the product of the two bf16 values (exact in fp32) rounded once.
+// e^-g is 2^(-g log2 e) on the hardware exp2 and the quotient a hardware
+// reciprocal times g: the fp32 silu is off by a relative (|g| + 4) 2^-23 at
+// most (the rounding of the exponent argument grows with |g|), far inside
+// the half-ulp of the bf16 rounding that follows (2^-9), so only values
+// within that distance of a bf16 rounding boundary can round the other way.
+// Past g < -88.7 the exponential overflows and silu(g) comes out -0 (exactly:
+// a negative number below 1e-36 in size); -inf gives NaN, as g / (1 + e^-g).
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+}
+__device__ __forceinline__ uint16_t swiglu_bf16(float acc_g, float acc_u) {
+  const float g = (float)(__bf16)acc_g;
+  const float u = (float)(__bf16)acc_u;
+  const float sl = (float)(__bf16)silu_f32(g);
+  const __bf16 h = (__bf16)(sl * u);
+  return __builtin_bit_cast(uint16_t, h);
+}
+// The same on two packed bf16 pairs (low half first): g and u already bf16.
+__device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t g2, uint32_t u2) {
+  const uint32_t s2 = pack_bf16x2(silu_f32(__uint_as_float(g2 << 16)),
+                                  silu_f32(__uint_as_float(g2 & 0xFFFF0000u)));
+  return pack_bf16x2(__uint_as_float(s2 << 16) * __uint_as_float(u2 << 16),
+                     __uint_as_float(s2 & 0xFFFF0000u) * __uint_as_float(u2 & 0xFFFF0000u));
+}
+
 }  // namespace fp8bl

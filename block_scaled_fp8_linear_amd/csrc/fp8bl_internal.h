@@ -44,8 +44,16 @@ size_t large_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_large(const uint16_t* x, const uint8_t* q, const float* s,
                              uint16_t* y, int64_t m, int64_t n, int64_t k,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+// Its gated form (gate/up pair, SwiGLU epilogue; N % 8 == 0, N < 2^21) and
+// that form's time estimate in the same units.
+double large_gated_cost(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_large_gated(const uint16_t* x, const uint8_t* qg, const float* sg,
+                                   const uint8_t* qu, const float* su, uint16_t* h, int64_t m,
+                                   int64_t n, int64_t k, hipStream_t stream);
 
-// MLP gate/up pair with the SwiGLU epilogue: h = swiglu(x Wg^T, x Wu^T).
+// MLP gate/up pair with the SwiGLU epilogue: h = swiglu(x Wg^T, x Wu^T), on
+// the tile-planned kernels; mlp_tiled_cost is their planner's estimate.
+double mlp_tiled_cost(int64_t m, int64_t n, int64_t k);
 hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
                               const uint8_t* qu, const float* su, uint16_t* h,
                               int64_t m, int64_t n, int64_t k, hipStream_t stream);

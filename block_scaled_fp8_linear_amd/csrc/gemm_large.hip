@@ -55,6 +55,13 @@
 //
 // Split-K (units with a K split): every split writes its fp32 partial tile to
 // the workspace and the ordered reduce kernel adds the splits and rounds once.
+//
+// Gated (the MLP gate/up pair with the SwiGLU epilogue): the tile covers 128
+// output columns; waves 0 and 1 run its gate weight rows and waves 2 and 3
+// the same rows of the up weight, everything else as above. Wave w and wave
+// w + 2 then hold the two products of one 256 x 64 output slice, element for
+// element, and finish half of it each after trading the other half through
+// LDS.
 #include <atomic>
 
 #include "fp8bl_device.h"
@@ -101,17 +108,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <bool SPLIT>
+// (q, s) is the weight; for GATED it is the gate weight and (q2, s2) the up
+// weight, and y receives the SwiGLU.
+template <bool SPLIT, bool GATED>
 __global__ __launch_bounds__(kThreads, 1)
 void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
-                       const float* __restrict__ s, uint16_t* __restrict__ y,
+                       const float* __restrict__ s, const uint8_t* __restrict__ q2,
+                       const float* __restrict__ s2, uint16_t* __restrict__ y,
                        float* __restrict__ part, int M, int N, int K, int gk,
                        int tiles_m, int tiles_n, int kt_per_split, int splits, int steps_per_unit) {
+  static_assert(!(SPLIT && GATED), "the SwiGLU needs whole sums: no K split");
   __shared__ __attribute__((aligned(1024))) uint16_t xs[kStages * kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Output columns of a tile, and the first row of this wave's weight rows
+  // within the tile's rows of its weight.
+  constexpr int kTileN = GATED ? kBN / 2 : kBN;
+  const int wrow = GATED ? 64 * (wave & 1) : 64 * wave;
+  const uint8_t* const wq = (GATED && wave >= 2) ? q2 : q;
+  const float* const wsc = (GATED && wave >= 2) ? s2 : s;
 
   // ---- Work units: (tile, K split) pairs, dealt to the persistent
   // workgroups round-robin (unit blockIdx.x + i * gridDim.x). Consecutive
@@ -138,7 +155,7 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     const int gsize = min(tiles_m - first_m, GM);
     const int in_group = id - group * GM * tiles_n;
     U.m0 = (first_m + in_group % gsize) * kBM;
-    U.n0 = (in_group / gsize) * kBN;
+    U.n0 = (in_group / gsize) * kTileN;
     U.kt0 = U.split * kt_per_split;
     U.nreal = min(kt_per_split, nkt - U.kt0);
     return U;
@@ -160,16 +177,17 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   for (int i = 0; i < kXLoads; ++i)
     xvo[i] = (uint32_t)((64 * wave + 8 * i + (lane >> 3)) * K * 2 + ((i & 1) ? xc_odd : xc_even) * 16);
   // codes: load i of wave w fills the stage's code rows 64w + 16i .. +16
-  // (64 bytes each, the step's K range); lane l lands on row (l / 4), physical
-  // 16-byte chunk l % 4, holding the logical chunk (l % 4) ^ (l / 16) (the
-  // row's (row / 4) % 4), so the decoding reads below are conflict-free.
-  // A wave loads, and later reads, only its own rows.
+  // (64 bytes each, the step's K range) from its weight rows wrow + 16i ..;
+  // lane l lands on row (l / 4), physical 16-byte chunk l % 4, holding the
+  // logical chunk (l % 4) ^ (l / 16) (the row's (row / 4) % 4), so the
+  // decoding reads below are conflict-free. A wave loads, and later reads,
+  // only its own rows.
   const int wc = (lane & 3) ^ (lane >> 4);
   uint32_t wvo[kWLoads];
 #pragma unroll
-  for (int i = 0; i < kWLoads; ++i) wvo[i] = (uint32_t)((64 * wave + 16 * i + (lane >> 2)) * K + 16 * wc);
+  for (int i = 0; i < kWLoads; ++i) wvo[i] = (uint32_t)((wrow + 16 * i + (lane >> 2)) * K + 16 * wc);
   const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc(s, (uint32_t)(((N + kBlock - 1) / kBlock) * gk * 4));
+      make_rsrc(wsc, (uint32_t)(((N + kBlock - 1) / kBlock) * gk * 4));
 
   // The unit whose steps are being loaded (two steps ahead of the one being
   // computed, so near the end of a unit it is the next one).
@@ -180,9 +198,9 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
   auto set_load_unit = [&](const Unit& U) {
     LU = U;
     xrs = make_rsrc(x + (size_t)U.m0 * K, (uint32_t)(U.nreal > 0 ? min(M - U.m0, kBM) * K * 2 : 0));
-    wrs = make_rsrc(q + (size_t)U.n0 * K, (uint32_t)(U.nreal > 0 ? max(min(N - U.n0, kBN), 0) * K : 0));
-    lwave_live = U.n0 + 64 * wave < N;
-    lsrow = lwave_live ? (U.n0 + 64 * wave) / kBlock : 0;
+    wrs = make_rsrc(wq + (size_t)U.n0 * K, (uint32_t)(U.nreal > 0 ? max(min(N - U.n0, kTileN), 0) * K : 0));
+    lwave_live = U.n0 + wrow < N;
+    lsrow = lwave_live ? (U.n0 + wrow) / kBlock : 0;
   };
   set_load_unit(LU);
 
@@ -402,7 +420,83 @@ void gemm_large_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     const Unit CU = unit_of(ci);
     const int rows = min(M - CU.m0, kBM);
     const int col_base = CU.n0 + col_lane;
-    if constexpr (!SPLIT) {
+    if constexpr (GATED) {
+      // Gate wave w < 2 finishes row blocks 0..3 of the slice and up wave
+      // w + 2 row blocks 4..7; each sends its partner the other four, rounded
+      // to bf16 (the SwiGLU rounds both products to bf16 first, so nothing
+      // is lost). Two rounds of two row blocks go through the sender's own
+      // 8 KB of X rows in the stage the last step used, 16 bytes per lane,
+      // lane-contiguous; a barrier after the writes hands them over, one
+      // after the partner's reads gives the rows back. Each finished row
+      // block then leaves as whole 128-byte lines through the same rows, as
+      // in the plain epilogue below. (Only N % 8 == 0 comes here.)
+      const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + (size_t)CU.m0 * N, (uint32_t)(rows * N * 2));
+      const int stage0 = (S == 0 ? 2 : S - 1) * kStageElems;
+      int le;
+      asm volatile("" : "=v"(le) : "0"(lane));
+      uint8_t* const own = reinterpret_cast<uint8_t*>(&xs[stage0 + wave * 64 * kBK]);
+      const uint8_t* const peer = reinterpret_cast<const uint8_t*>(&xs[stage0 + (wave ^ 2) * 64 * kBK]);
+      const bool up = wave >= 2;
+      const int er = le & 31, eh = le >> 5;
+      const int rr = le >> 3;
+      const int col8 = CU.n0 + wrow + 8 * (le & 7);
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const f32x16 a = up ? acc[nb][2 * r2 + i] : acc[nb][4 + 2 * r2 + i];
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              u32x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(a[8 * gp + 2 * e], a[8 * gp + 2 * e + 1]);
+              *reinterpret_cast<u32x4*>(own + ((2 * i + nb) * 2 + gp) * 1024 + le * 16) = v;
+            }
+          }
+        __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+        wg_barrier();
+        u32x4 got[2][2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp)
+              got[i][nb][gp] = *reinterpret_cast<const u32x4*>(peer + ((2 * i + nb) * 2 + gp) * 1024 + le * 16);
+        __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+        wg_barrier();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          uint8_t* const buf = own + i * 4096;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const f32x16 a = up ? acc[nb][4 + 2 * r2 + i] : acc[nb][2 * r2 + i];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              u32x2 v;
+#pragma unroll
+              for (int w2 = 0; w2 < 2; ++w2) {
+                const uint32_t mine = pack_bf16x2(a[4 * g + 2 * w2], a[4 * g + 2 * w2 + 1]);
+                const uint32_t theirs = got[i][nb][g >> 1][2 * (g & 1) + w2];
+                v[w2] = swiglu_bf16x2(up ? theirs : mine, up ? mine : theirs);
+              }
+              const int chunk = (4 * nb + g) ^ ((er >> 1) & 7);
+              *reinterpret_cast<u32x2*>(buf + er * 128 + chunk * 16 + 8 * eh) = v;
+            }
+          }
+          const int mb = (up ? 4 : 0) + 2 * r2 + i;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 8 * j + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(buf + r * 128 + (((le & 7) ^ ((r >> 1) & 7)) * 16));
+            const uint32_t off = col8 < N ? (uint32_t)(((32 * mb + r) * N + col8) * 2) : kOob;
+            __builtin_amdgcn_raw_buffer_store_b128(v, yrs, off, 0, 0);
+          }
+        }
+      }
+    } else if constexpr (!SPLIT) {
       const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + (size_t)CU.m0 * N, (uint32_t)(rows * N * 2));
       if ((N & 3) == 0) {
         if ((N & 7) == 0) {
@@ -612,19 +706,48 @@ hipError_t launch_gemm_large(const uint16_t* x, const uint8_t* q, const float* s
   const int grid = units < device_cus() ? units : device_cus();
   const int spu = p.kt_per_split > 2 ? p.kt_per_split : 2;
   if (p.splits == 1) {
-    hipLaunchKernelGGL(gemm_large_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                       x, q, s, y, nullptr, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
-                       p.kt_per_split, 1, spu);
+    hipLaunchKernelGGL((gemm_large_kernel<false, false>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                       stream, x, q, s, nullptr, nullptr, y, nullptr, (int)m, (int)n, (int)k, gk,
+                       tiles_m, tiles_n, p.kt_per_split, 1, spu);
     return hipGetLastError();
   }
   if (ws == nullptr || ws_bytes < large_workspace_bytes(m, n, k)) return hipErrorInvalidValue;
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL(gemm_large_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                     x, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
-                     p.kt_per_split, p.splits, spu);
+  hipLaunchKernelGGL((gemm_large_kernel<true, false>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                     stream, x, q, s, nullptr, nullptr, y, part, (int)m, (int)n, (int)k, gk,
+                     tiles_m, tiles_n, p.kt_per_split, p.splits, spu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce_partials(part, y, p.splits, m, n, stream);
+}
+
+// The gated form's tiles are 256 x 128 outputs, each the work of a plain
+// 256 x 256 tile, never split: the plain model at one split, with the rate
+// measured on the gate/up pair at 512 and 768 rows (2.7 steps per
+// microsecond per CU; the 2.42 above is from 16384 rows, where the chip runs
+// at lower clocks). Against the tiled gate/up planner it picked the faster
+// kernel on all seven shapes measured (128 to 4096 rows).
+double large_gated_cost(int64_t m, int64_t n, int64_t k) {
+  const int nkt = (int)((k + kBK - 1) / kBK);
+  const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN / 2 - 1) / (kBN / 2));
+  return (double)((tiles + 255) / 256) * (nkt * 4 / 2.7 + 2.0);
+}
+
+hipError_t launch_gemm_large_gated(const uint16_t* x, const uint8_t* qg, const float* sg,
+                                   const uint8_t* qu, const float* su, uint16_t* h, int64_t m,
+                                   int64_t n, int64_t k, hipStream_t stream) {
+  if ((n & 7) != 0) return hipErrorInvalidValue;
+  const int nkt = (int)((k + kBK - 1) / kBK);
+  const int gk = (int)((k + kBlock - 1) / kBlock);
+  const int tiles_m = (int)((m + kBM - 1) / kBM);
+  const int tiles_n = (int)((n + kBN / 2 - 1) / (kBN / 2));
+  const int units = tiles_m * tiles_n;
+  const int grid = units < device_cus() ? units : device_cus();
+  const int spu = nkt > 2 ? nkt : 2;
+  hipLaunchKernelGGL((gemm_large_kernel<false, true>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                     stream, x, qg, sg, qu, su, h, nullptr, (int)m, (int)n, (int)k, gk, tiles_m,
+                     tiles_n, nkt, 1, spu);
+  return hipGetLastError();
 }
 
 }  // namespace fp8bl

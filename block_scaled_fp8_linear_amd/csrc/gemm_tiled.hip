@@ -85,18 +85,6 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// bf16 SwiGLU of two fp32 accumulators, rounded where eager bf16 ops round
-// (FastVideo fasth3_omniref_b200 README, "What --lossless-accel turns on"):
-// g and u each to bf16, silu(g) = g / (1 + e^-g) in fp32 then to bf16, and
-// the product of the two bf16 values (exact in fp32) rounded once.
-__device__ __forceinline__ uint16_t swiglu_bf16(float acc_g, float acc_u) {
-  const float g = (float)(__bf16)acc_g;
-  const float u = (float)(__bf16)acc_u;
-  const float sl = (float)(__bf16)(g / (1.0f + expf(-g)));
-  const __bf16 h = (__bf16)(sl * u);
-  return __builtin_bit_cast(uint16_t, h);
-}
-
 // Order of a step's MFMA phase: the X fragment reads (one ds_read_b128 per
 // fragment, 4 * MB per step) run kReadsAhead fragments in front of the MFMAs
 // that consume them, each fragment feeding PER_FRAG MFMAs. Left to itself
@@ -569,12 +557,42 @@ hipError_t launch_gemm_tiled(const uint16_t* x, const uint8_t* q, const float* s
 // 1024-1536 rows (one shape within 1% the other way); the two-weight tile
 // is 2-6% faster from 2048 rows. An eight-wave 128x256
 // tile with both weights in every wave measured slower than both.
+namespace {
+
+// The gate/up planner's choice: 0 = two-weight tile, 1 = 256-row paired tile,
+// 2 = 128-row paired tile; its time estimate (planner units) in *cost.
+int plan_mlp(int64_t m, int64_t n, int64_t k, double* cost) {
+  const int64_t nkt = (k + 63) / 64;
+  const int64_t tiles_n = (n + 127) / 128;
+  if (m >= 2048) {
+    const int64_t per_cu = ((m + 127) / 128 * tiles_n + 511) / 512;
+    *cost = (double)(per_cu * nkt) * 4 / 2.0;
+    return 0;
+  }
+  const int64_t per_cu256 = ((m + 255) / 256 * tiles_n + 255) / 256;
+  const int64_t per_cu128 = ((m + 127) / 128 * tiles_n + 255) / 256;
+  const double cost256 = (double)per_cu256 * 4 / 2.2;
+  const double cost128 = (double)per_cu128 * 2 / (per_cu128 <= 1 ? 1.51 : 2.09);
+  *cost = (double)nkt * (cost256 < cost128 ? cost256 : cost128);
+  return cost256 < cost128 ? 1 : 2;
+}
+
+}  // namespace
+
+double mlp_tiled_cost(int64_t m, int64_t n, int64_t k) {
+  double c = 0;
+  plan_mlp(m, n, k, &c);
+  return c;
+}
+
 hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float* sg,
                               const uint8_t* qu, const float* su, uint16_t* h,
                               int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const int gk = (int)((k + kBlock - 1) / kBlock);
   const int tiles_n = (int)((n + 127) / 128);
-  if (m >= 2048) {
+  double cost = 0;
+  const int kind = plan_mlp(m, n, k, &cost);
+  if (kind == 0) {
     const int tiles_m = (int)((m + 127) / 128);
     hipLaunchKernelGGL((gemm_gated_kernel<128, 128, 2>), dim3((uint32_t)(tiles_m * tiles_n), 1),
                        dim3(kThreads), 0, stream, x, qg, sg, qu, su, h, (int)m, (int)n, (int)k,
@@ -582,11 +600,7 @@ hipError_t launch_mlp_gate_up(const uint16_t* x, const uint8_t* qg, const float*
     return hipGetLastError();
   }
   const int tm256 = (int)((m + 255) / 256), tm128 = (int)((m + 127) / 128);
-  const int64_t per_cu256 = ((int64_t)tm256 * tiles_n + 255) / 256;
-  const int64_t per_cu128 = ((int64_t)tm128 * tiles_n + 255) / 256;
-  const double cost256 = (double)per_cu256 * 4 / 2.2;
-  const double cost128 = (double)per_cu128 * 2 / (per_cu128 <= 1 ? 1.51 : 2.09);
-  if (cost256 < cost128)
+  if (kind == 1)
     hipLaunchKernelGGL((gemm_gated_paired_kernel<256, 256, 1>),
                        dim3((uint32_t)(tm256 * tiles_n), 1), dim3(512), 0, stream, x, qg, sg, qu,
                        su, h, (int)m, (int)n, (int)k, gk, tm256, tiles_n);

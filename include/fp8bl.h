@@ -161,6 +161,17 @@ int fp8_block_mlp_gate_up(const uint16_t* x, const uint8_t* q_gate, const float*
                           const uint8_t* q_up, const float* scale_inv_up, uint16_t* h,
                           int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+/* fp8_block_mlp_gate_up with the kernel named: FP8BL_PATH_AUTO (what
+ * fp8_block_mlp_gate_up does: the lower of two cost-model estimates),
+ * FP8BL_PATH_TILED (the tile-planned gate/up kernels) or FP8BL_PATH_LARGE
+ * (the large-M kernel's gated form: 256 x 128 output tiles, gate and up rows
+ * in separate waves; needs n % 8 == 0 and n < 2^21). Any other path value,
+ * or LARGE with another n, is FP8BL_INVALID_ARG. Both kernels meet the same
+ * bound; their h may differ in the last bit where their fp32 sums do. */
+int fp8_block_mlp_gate_up_ex(const uint16_t* x, const uint8_t* q_gate, const float* scale_inv_gate,
+                             const uint8_t* q_up, const float* scale_inv_up, uint16_t* h,
+                             int64_t m, int64_t n, int64_t k, int path, hipStream_t stream);
+
 /* ---- W8A8 route -------------------------------------------------------
  * FastVideo PR #1829, "Changes", first bullet: the Blackwell route pairs a
  * groupwise FP8 GEMM with a (Triton) quantizer. Read here as: activations

@@ -20,7 +20,7 @@ def test_header_symbols_exported(lib):
         "fp8_block_abi_version", "fp8_block_status_string", "fp8_block_device_supported",
         "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
         "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
-        "fp8_block_mlp_gate_up", "fp8_act_quantize", "fp8_block_linear_w8a8_workspace_size",
+        "fp8_block_mlp_gate_up", "fp8_block_mlp_gate_up_ex", "fp8_act_quantize", "fp8_block_linear_w8a8_workspace_size",
         "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16", "fp8_block_stream_read",
         "fp8_block_linear_noalloc",
     }
@@ -120,6 +120,24 @@ def test_noalloc_scratch_size_matches_header():
 ])
 def test_mlp_gate_up_argument_errors(lib, args, status):
     assert L.mlp_gate_up_raw(*args) == status
+    # the kernel-choosing form checks the same way on each path that takes the shape
+    for path in (L.PATH_AUTO, L.PATH_TILED) + ((L.PATH_LARGE,) if args[7] % 8 == 0 else ()):
+        assert L.mlp_gate_up_ex_raw(*args, path) == status
+
+
+@pytest.mark.parametrize("n,path,status", [
+    (8, 2, L.FP8BL_INVALID_ARG),          # SKINNY is not a gate/up kernel
+    (8, 4, L.FP8BL_INVALID_ARG),          # unknown path
+    (8, -1, L.FP8BL_INVALID_ARG),
+    (12, L.PATH_LARGE, L.FP8BL_INVALID_ARG),   # the large kernel needs N % 8 == 0
+    (1 << 21, L.PATH_LARGE, L.FP8BL_INVALID_ARG),
+    (12, L.PATH_TILED, L.FP8BL_OK),
+])
+def test_mlp_gate_up_ex_paths(lib, n, path, status):
+    """Path checks come before any device work (M = 0 here: a valid call
+    returns at once)."""
+    args = (FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 8 * FAKE, 0, n, 16)
+    assert L.mlp_gate_up_ex_raw(*args, path) == status
 
 
 @pytest.mark.parametrize("m,k,xoff,qoff,soff,status", [

@@ -23,8 +23,9 @@ pytestmark = [
 import block_scaled_fp8_linear_amd as F  # noqa: E402
 
 
-def run_mlp(x_bits, qg, sg, qu, su):
-    h = F.fp8_block_mlp_gate_up(to_bf16(x_bits), to_u8(qg), to_f32(sg), to_u8(qu), to_f32(su))
+def run_mlp(x_bits, qg, sg, qu, su, path=F.PATH_AUTO):
+    h = F.fp8_block_mlp_gate_up(to_bf16(x_bits), to_u8(qg), to_f32(sg), to_u8(qu), to_f32(su),
+                                path=path)
     torch.cuda.synchronize()
     return bits(h)
 
@@ -46,6 +47,39 @@ def _check_full(x, qg, sg, qu, su, h, label):
     assert worst <= 1.0, (label, worst, np.unravel_index(np.argmax(r), r.shape))
 
 
+# The kernels evaluate silu in fp32 with the hardware exp2 and reciprocal:
+# relative error at most (|g| + 4) 2^-23, below 2^-16 for every g >= -87. Past
+# about -87 the exponential overflows fp32 and silu comes out as zero.
+SILU_REL = 2.0 ** -16
+SILU_ZERO_BELOW = -87.0
+
+
+def _swiglu_consistent(h, g_bits, u_bits):
+    """Where h can differ from the oracle's SwiGLU of the same bf16 g and u:
+    only through the bf16 rounding of silu(g), which may land on the other
+    neighbour when silu(g) is within SILU_REL of a rounding boundary. True
+    where h is bf16(s' u) for s' a bf16 rounding of a value within SILU_REL of
+    the exact silu(g), or zero for g below SILU_ZERO_BELOW."""
+    g = O.bf16_bits_to_f32(g_bits).astype(np.float64)
+    u = O.bf16_bits_to_f32(u_bits)
+    sil = O.silu_exact(g)
+    ok = np.zeros(h.shape, dtype=bool)
+    for f in (1.0 - SILU_REL, 1.0 + SILU_REL):
+        sb = O.bf16_rne_bits((sil * f).astype(np.float32))
+        ok |= h == O.bf16_rne_bits(O.bf16_bits_to_f32(sb) * u)
+    ok |= (g < SILU_ZERO_BELOW) & ((h & 0x7FFF) == 0)
+    return ok
+
+
+def _check_against_linears(h, g, u, label):
+    ref = O.swiglu_bf16(g, u)
+    differ = int((h != ref).sum())
+    say(label, "differing from the SwiGLU of the two linears:", differ, "of", h.size)
+    assert differ <= 1e-4 * h.size
+    ok = _swiglu_consistent(h, g, u)
+    assert ok.all(), (label, np.argwhere(~ok)[:5])
+
+
 @pytest.mark.parametrize("m,n,k", [
     (1, 8, 16), (5, 130, 48), (37, 200, 272), (64, 384, 256),
     (130, 300, 1040), (256, 256, 512), (300, 520, 784),
@@ -63,12 +97,51 @@ def test_mlp_small_shapes(m, n, k):
 ])
 def test_mlp_larger_shapes_each_kernel(m, n, k):
     """Ragged shapes (partial row and column tiles, K not a multiple of 64)
-    that the gate/up planner sends to the kernels the small shapes above do
-    not reach, compared in full."""
+    that the tiled gate/up planner sends to the kernels the small shapes
+    above do not reach, compared in full."""
     x, qg, sg, qu, su = _pair(m + 3 * n + k, m, n, k)
-    say("mlp gate/up", m, n, k)
-    h = run_mlp(x, qg, sg, qu, su)
-    _check_full(x, qg, sg, qu, su, h, f"mlp {m}x{n}x{k}")
+    say("mlp gate/up tiled", m, n, k)
+    h = run_mlp(x, qg, sg, qu, su, F.PATH_TILED)
+    _check_full(x, qg, sg, qu, su, h, f"mlp tiled {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 8, 16),            # one row, one partial column tile, one K chunk
+    (37, 200, 272),        # ragged everything; the second wave pair past N
+    (256, 256, 512),       # exact tiles
+    (300, 520, 784),       # partial row and column tiles, K % 64 = 16
+    (700, 1032, 1040),     # several units per workgroup's walk, N % 128 = 8
+    (2100, 384, 3088),     # many steps, the last one partial
+])
+def test_mlp_large_kernel_shapes(m, n, k):
+    """The large kernel's gated form (N % 8 == 0), compared in full."""
+    x, qg, sg, qu, su = _pair(m * 5 + n + k, m, n, k)
+    say("mlp gate/up large", m, n, k)
+    h = run_mlp(x, qg, sg, qu, su, F.PATH_LARGE)
+    _check_full(x, qg, sg, qu, su, h, f"mlp large {m}x{n}x{k}")
+
+
+def test_mlp_large_matches_large_linears():
+    """At a shape where the large kernel's plain form does not split K, its g
+    and u are the gated form's g and u bit for bit (same tile rows, same K
+    order), so h must be the SwiGLU of the two plain outputs up to silu's fp32
+    evaluation: equal almost everywhere, never more than one bf16 ulp off.
+    The shape has partial row and column tiles."""
+    m, n, k = 1000, 4088, 768
+    x, qg, sg, qu, su = _pair(12, m, n, k)
+    say("mlp large vs large linears", m, n, k)
+    h = run_mlp(x, qg, sg, qu, su, F.PATH_LARGE)
+    g = bits(F.fp8_block_linear(to_bf16(x), to_u8(qg), to_f32(sg), path=F.PATH_LARGE))
+    u = bits(F.fp8_block_linear(to_bf16(x), to_u8(qu), to_f32(su), path=F.PATH_LARGE))
+    _check_against_linears(h, g, u, "mlp large vs large linears")
+
+
+def test_mlp_large_path_rejects_ragged_n():
+    x, qg, sg, qu, su = _pair(5, 64, 132, 128)
+    with pytest.raises(F.Fp8blError):
+        run_mlp(x, qg, sg, qu, su, F.PATH_LARGE)
+    with pytest.raises(F.Fp8blError):
+        run_mlp(x, qg, sg, qu, su, F.PATH_SKINNY)
 
 
 def test_mlp_matches_separate_linears():
@@ -76,21 +149,54 @@ def test_mlp_matches_separate_linears():
     fused kernel's g and u bit for bit (every tile shape accumulates an output
     in the same order), so the
     fused h must be the SwiGLU of the two plain outputs up to silu's fp32
-    evaluation: equal almost everywhere, never more than one bf16 ulp off."""
+    evaluation: equal almost everywhere, and elsewhere only where the bf16
+    rounding of silu can go the other way."""
     m, n, k = 1024, 4096, 1024
     x, qg, sg, qu, su = _pair(11, m, n, k)
     say("mlp vs separate linears", m, n, k)
-    h = run_mlp(x, qg, sg, qu, su)
+    h = run_mlp(x, qg, sg, qu, su, F.PATH_TILED)
     g = bits(F.fp8_block_linear(to_bf16(x), to_u8(qg), to_f32(sg), path=F.PATH_TILED))
     u = bits(F.fp8_block_linear(to_bf16(x), to_u8(qu), to_f32(su), path=F.PATH_TILED))
+    _check_against_linears(h, g, u, "mlp tiled vs tiled linears")
+
+
+@pytest.mark.parametrize("path", ["tiled", "large"])
+def test_mlp_silu_values(path):
+    """silu pinned value by value: x picks one column of each weight (x[i, i]
+    = 1), the up weight is all ones there, so h[i, j] is bf16(silu(g)) of
+    g = the gate weight's dequantized element (j, i). The gate codes run
+    through every finite E4M3 code, under eight scales from 2^-9 to 2^5 (and
+    two that are not powers of two), so g spans about +-1e-5 .. +-1.4e4,
+    the exponential's overflow below -87 included."""
+    m, n, k = 4, 1024, 128
+    j = np.arange(n)[:, None]
+    c = np.arange(k)[None, :]
+    codes = ((4 * j + c) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0            # no NaN codes
+    qg = np.where(c < m, codes, 0).astype(np.uint8)
+    sg = np.array([[2.0 ** -9], [2.0 ** -6], [2.0 ** -3], [1.0], [3.7], [2.0 ** 3],
+                   [2.0 ** 5], [0.013]], dtype=np.float32)
+    qu = np.where(c < m, 0x38, 0).astype(np.uint8).repeat(n, axis=0)   # E4M3 1.0
+    su = np.ones((n // 128, 1), dtype=np.float32)
+    x = np.zeros((m, k), dtype=np.uint16)
+    x[np.arange(m), np.arange(m)] = 0x3F80                               # bf16 1.0
+    say("mlp silu values", path)
+    h = run_mlp(x, qg, sg, qu, su, F.PATH_LARGE if path == "large" else F.PATH_TILED)
+    # g from the oracle's product: the one nonzero term, exact in bf16 (a -0
+    # weight element sums with the zero terms to +0)
+    g = O.bf16_rne_bits(O.linear_value(x, O.dequant(qg, sg)).astype(np.float32))
+    u = np.full(h.shape, 0x3F80, dtype=np.uint16)
+    gv = O.bf16_bits_to_f32(g)
+    say("g range", float(gv.min()), float(gv.max()), "overflow cases", int((gv < SILU_ZERO_BELOW).sum()))
+    assert gv.min() < SILU_ZERO_BELOW and gv.max() > 1e4
+    ok = _swiglu_consistent(h, g, u)
+    assert ok.all(), np.argwhere(~ok)[:5]
     ref = O.swiglu_bf16(g, u)
-    diff = np.abs(h.astype(np.int32) - ref.astype(np.int32))
-    same_sign = (h >> 15) == (ref >> 15)
-    say("mlp vs separate: differing", int((diff != 0).sum()), "of", diff.size)
-    assert (diff != 0).mean() < 1e-3
-    both_zero = ((h & 0x7FFF) == 0) & ((ref & 0x7FFF) == 0)
-    one_ulp = (diff <= 1) & same_sign
-    assert np.all(one_ulp | both_zero)
+    live = gv >= SILU_ZERO_BELOW
+    say("silu values off the oracle's rounding", int((h != ref)[live].sum()), "of", int(live.sum()))
+    # (a CPU emulation of the kernels' fp32 silu puts 10 of these 4096 on the
+    # other rounding: the large-|g| cases, where the exponent's rounding counts)
+    assert (h != ref)[live].sum() <= 0.01 * live.sum()
 
 
 def test_mlp_zero_input_and_zero_weight():
