@@ -60,7 +60,8 @@ LAUNCH_KERNELS = {
               "+ reduce_partials_kernel when K is split",
     "dequant": "fp8_block_dequant: dequant_kernel",
     "quantize": "fp8_block_quantize: quantize_kernel<float>",
-    "mlp": "fp8_block_mlp_gate_up: gemm_gated_paired_kernel (below 2048 rows) or gemm_gated_kernel",
+    "mlp": "fp8_block_mlp_gate_up: gemm_large_kernel<false, true> (the gated form), or on the tiled "
+           "planner's pick gemm_gated_paired_kernel (below 2048 rows) or gemm_gated_kernel",
     "w8a8": "fp8_block_linear_w8a8_bf16: act_quantize_kernel + gemm_w8a8_kernel, "
             "+ reduce_partials_kernel when K is split",
     "w8a8_gemm": "fp8_block_linear_w8a8: gemm_w8a8_kernel, + reduce_partials_kernel when K is split",
