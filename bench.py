@@ -62,9 +62,10 @@ LAUNCH_KERNELS = {
     "quantize": "fp8_block_quantize: quantize_kernel<float>",
     "mlp": "fp8_block_mlp_gate_up: gemm_large_kernel<false, true> (the gated form), or on the tiled "
            "planner's pick gemm_gated_paired_kernel (below 2048 rows) or gemm_gated_kernel",
-    "w8a8": "fp8_block_linear_w8a8_bf16: act_quantize_kernel + gemm_w8a8_kernel, "
-            "+ reduce_partials_kernel when K is split",
-    "w8a8_gemm": "fp8_block_linear_w8a8: gemm_w8a8_kernel, + reduce_partials_kernel when K is split",
+    "w8a8": "fp8_block_linear_w8a8_bf16: act_quantize_kernel + gemm_w8a8_large_kernel or "
+            "gemm_w8a8_kernel, + reduce_partials_kernel when K is split",
+    "w8a8_gemm": "fp8_block_linear_w8a8: gemm_w8a8_large_kernel or gemm_w8a8_kernel, "
+                 "+ reduce_partials_kernel when K is split",
 }
 
 
@@ -82,6 +83,7 @@ KERNEL_SOURCES = {
     "quantize_kernel": ("quantize.hip",),
     "act_quantize_kernel": ("quantize.hip",),
     "gemm_w8a8_kernel": ("gemm_w8a8.hip",),
+    "gemm_w8a8_large_kernel": ("gemm_w8a8_large.hip",),
     "stream_read_kernel": ("stream_read.hip",),
 }
 SHARED_SOURCES = ("fp8bl_api.hip", "fp8bl_device.h", "fp8bl_internal.h")

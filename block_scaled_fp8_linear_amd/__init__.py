@@ -238,8 +238,11 @@ def _w8a8_workspace(m, n, k, workspace, dev):
 
 def fp8_block_linear_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, q: torch.Tensor,
                           s: torch.Tensor, out: torch.Tensor | None = None,
-                          workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """E4M3 xq [M,K] + x_scale [ceil(K/128), M], block-FP8 weight -> bf16 y [M,N]."""
+                          workspace: torch.Tensor | None = None,
+                          path: int = PATH_AUTO) -> torch.Tensor:
+    """E4M3 xq [M,K] + x_scale [ceil(K/128), M], block-FP8 weight -> bf16 y [M,N].
+    ``path``: PATH_AUTO, PATH_TILED (128x128 tiles) or PATH_LARGE (256x256
+    tiles, N % 8 == 0)."""
     _need(xq, torch.uint8, "xq")
     _need(x_scale, torch.float32, "x_scale")
     _need(q, torch.uint8, "q")
@@ -259,9 +262,9 @@ def fp8_block_linear_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, q: torch.Tens
         raise ValueError("out shape")
     workspace, ws_ptr, ws_bytes = _w8a8_workspace(m, n, k, workspace, xq.device)
     with torch.cuda.device(xq.device):
-        _check(_lib.linear_w8a8_raw(xq.data_ptr(), x_scale.data_ptr(), q.data_ptr(), s.data_ptr(),
-                                    out.data_ptr(), m, n, k, ws_ptr, ws_bytes,
-                                    _stream(xq.device)), "fp8_block_linear_w8a8")
+        _check(_lib.linear_w8a8_ex_raw(xq.data_ptr(), x_scale.data_ptr(), q.data_ptr(),
+                                       s.data_ptr(), out.data_ptr(), m, n, k, ws_ptr, ws_bytes,
+                                       int(path), _stream(xq.device)), "fp8_block_linear_w8a8")
     return out
 
 

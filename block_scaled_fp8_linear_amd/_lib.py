@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.fp8_block_linear_w8a8_workspace_size.argtypes = [i64, i64, i64]
     lib.fp8_block_linear_w8a8.restype = c_int
     lib.fp8_block_linear_w8a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    lib.fp8_block_linear_w8a8_ex.restype = c_int
+    lib.fp8_block_linear_w8a8_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, c_int, vp]
     lib.fp8_block_linear_w8a8_bf16.restype = c_int
     lib.fp8_block_linear_w8a8_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
     lib.fp8_block_quantize.restype = c_int
@@ -148,6 +150,11 @@ def w8a8_workspace_size(m: int, n: int, k: int) -> int:
 def linear_w8a8_raw(xq: int, xs: int, q: int, s: int, y: int, m: int, n: int, k: int,
                     ws: int, ws_bytes: int, stream: int = 0) -> int:
     return load().fp8_block_linear_w8a8(xq, xs, q, s, y, m, n, k, ws, ws_bytes, stream)
+
+
+def linear_w8a8_ex_raw(xq: int, xs: int, q: int, s: int, y: int, m: int, n: int, k: int,
+                       ws: int, ws_bytes: int, path: int, stream: int = 0) -> int:
+    return load().fp8_block_linear_w8a8_ex(xq, xs, q, s, y, m, n, k, ws, ws_bytes, path, stream)
 
 
 def linear_w8a8_bf16_raw(x: int, q: int, s: int, y: int, m: int, n: int, k: int,

@@ -46,8 +46,18 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file device code generation options. The W8A8 large-tile kernel keeps
+# its 192 accumulators in VGPRs and scales each MFMA block sum with a VALU
+# FMA: the VGPR form of the MFMA puts those sums where the FMA can read them
+# (the default AGPR form costs a copy per value, doubling the VALU work).
+FILE_FLAGS = {
+    "gemm_w8a8_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [hipcc(), *COMMON_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -344,10 +344,13 @@ FP8BL_EXPORT size_t fp8_block_linear_w8a8_workspace_size(int64_t m, int64_t n, i
   return w8a8_act_bytes(m, k) + fp8bl::w8a8_partials_bytes(m, n, k);
 }
 
-FP8BL_EXPORT int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t* q,
-                                       const float* scale_inv, uint16_t* y, int64_t m, int64_t n,
-                                       int64_t k, void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+FP8BL_EXPORT int fp8_block_linear_w8a8_ex(const uint8_t* xq, const float* x_scale,
+                                          const uint8_t* q, const float* scale_inv, uint16_t* y,
+                                          int64_t m, int64_t n, int64_t k, void* workspace,
+                                          size_t workspace_bytes, int path, hipStream_t stream) {
+  if (path != FP8BL_PATH_AUTO && path != FP8BL_PATH_TILED && path != FP8BL_PATH_LARGE)
+    return FP8BL_INVALID_ARG;
+  if (path == FP8BL_PATH_LARGE && (n % 8 != 0 || n >= kLargeMaxN)) return FP8BL_INVALID_ARG;
   int st = validate_w8a8(xq, x_scale, q, scale_inv, y, m, n, k);
   if (st != FP8BL_OK) return st;
   if (m == 0 || n == 0) return FP8BL_OK;
@@ -363,8 +366,19 @@ FP8BL_EXPORT int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, 
   }
   st = gate_current_device();
   if (st != FP8BL_OK) return st;
+  const int kind = path == FP8BL_PATH_AUTO    ? (n < kLargeMaxN ? fp8bl::w8a8_choose(m, n, k) : 0)
+                   : path == FP8BL_PATH_LARGE ? 1
+                                              : 0;
   return hip_status(fp8bl::launch_gemm_w8a8(xq, x_scale, q, scale_inv, y, m, n, k, workspace,
-                                            workspace_bytes, stream));
+                                            workspace_bytes, stream, kind));
+}
+
+FP8BL_EXPORT int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t* q,
+                                       const float* scale_inv, uint16_t* y, int64_t m, int64_t n,
+                                       int64_t k, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  return fp8_block_linear_w8a8_ex(xq, x_scale, q, scale_inv, y, m, n, k, workspace,
+                                  workspace_bytes, FP8BL_PATH_AUTO, stream);
 }
 
 FP8BL_EXPORT int fp8_block_linear_w8a8_bf16(const uint16_t* x, const uint8_t* q,
@@ -390,7 +404,8 @@ FP8BL_EXPORT int fp8_block_linear_w8a8_bf16(const uint16_t* x, const uint8_t* q,
   hipError_t e = fp8bl::launch_act_quantize(x, xq, xs, m, k, stream);
   if (e != hipSuccess) return FP8BL_HIP_ERROR;
   return hip_status(fp8bl::launch_gemm_w8a8(xq, xs, q, scale_inv, y, m, n, k, part,
-                                            need - w8a8_act_bytes(m, k), stream));
+                                            need - w8a8_act_bytes(m, k), stream,
+                                            n < kLargeMaxN ? fp8bl::w8a8_choose(m, n, k) : 0));
 }
 
 FP8BL_EXPORT int fp8_block_quantize(const float* w, uint8_t* q, float* scale_inv,

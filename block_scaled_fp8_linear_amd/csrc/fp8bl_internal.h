@@ -20,10 +20,22 @@ hipError_t launch_quantize_bf16(const uint16_t* w, uint8_t* q, float* s,
 // FP8 x FP8 block-scaled GEMM.
 hipError_t launch_act_quantize(const uint16_t* x, uint8_t* xq, float* xs, int64_t m, int64_t k,
                                hipStream_t stream);
+// W8A8 kernels: `kind` 0 = 128x128 tiles, 1 = 256x256 tiles (N % 8 == 0),
+// -1 = the cost models' choice. w8a8_partials_bytes covers either kernel.
 size_t w8a8_partials_bytes(int64_t m, int64_t n, int64_t k);
+int w8a8_choose(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const float* s,
                             uint16_t* y, int64_t m, int64_t n, int64_t k, void* ws,
-                            size_t ws_bytes, hipStream_t stream);
+                            size_t ws_bytes, hipStream_t stream, int kind = -1);
+struct W8a8LargePlan {
+  int splits, kb_per_split;
+  double cost;      // time estimate, microseconds
+};
+W8a8LargePlan plan_w8a8_large(int64_t m, int64_t n, int64_t k);
+size_t w8a8_large_partials_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_w8a8_large(const uint8_t* xq, const float* xs, const uint8_t* q,
+                                  const float* s, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Tile-planned fused GEMM (E4M3 tiles decoded to bf16 in registers, bf16
 // MFMA); tiled_cost is its planner's time estimate for the chosen plan.

@@ -279,6 +279,7 @@ void gemm_w8a8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ 
 
 struct W8a8Plan {
   int splits, kb_per_split;
+  double cost;      // time estimate, microseconds
 };
 
 // Split K (in 128-wide blocks) only when there are fewer tiles than CUs,
@@ -287,23 +288,30 @@ struct W8a8Plan {
 W8a8Plan plan_w8a8(int64_t m, int64_t n, int64_t k) {
   const int gk = (int)((k + kTile - 1) / kTile);
   const int64_t tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
+  // one 128x128x128 step of a workgroup, two workgroups per CU: 0.73 us
+  // each (measured on 16384x3072x3072, 16384x12288x3072 and 4096^3)
+  constexpr double kStepUs = 0.73;
+  auto cost_of = [&](int sp) {
+    const int steps = (gk + sp - 1) / sp;
+    const int64_t w = tiles * sp;
+    const double load = w <= 256 ? 1.67 : (double)((w + 255) / 256);
+    double cost = load * steps * kStepUs;
+    if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
+    return cost;
+  };
   int splits = 1;
+  double best = cost_of(1);
   if (tiles < 256) {
-    const double kStepUs = 0.5;          // one 128x128x128 step, two workgroups per CU
-    double best = 1e30;
-    for (int sp = 1; sp <= 8; ++sp) {
-      const int steps = (gk + sp - 1) / sp;
-      if (sp > 1 && steps < 4) break;
-      const int64_t w = tiles * sp;
-      const double load = w <= 256 ? 1.67 : (double)((w + 255) / 256);
-      double cost = load * steps * kStepUs;
-      if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
+    for (int sp = 2; sp <= 8; ++sp) {
+      if ((gk + sp - 1) / sp < 4) break;
+      const double cost = cost_of(sp);
       if (cost < best) { best = cost; splits = sp; }
     }
   }
   W8a8Plan p;
   p.kb_per_split = (gk + splits - 1) / splits;
   p.splits = (gk + p.kb_per_split - 1) / p.kb_per_split;
+  p.cost = best;
   return p;
 }
 
@@ -311,13 +319,26 @@ W8a8Plan plan_w8a8(int64_t m, int64_t n, int64_t k) {
 
 size_t w8a8_partials_bytes(int64_t m, int64_t n, int64_t k) {
   const W8a8Plan p = plan_w8a8(m, n, k);
-  if (p.splits <= 1) return 0;
-  return round_up((size_t)p.splits * partial_slab(m, n) * sizeof(float), kWorkspaceAlign);
+  const size_t own = p.splits <= 1 ? 0
+                   : round_up((size_t)p.splits * partial_slab(m, n) * sizeof(float), kWorkspaceAlign);
+  const size_t large = (n % 8 == 0) ? w8a8_large_partials_bytes(m, n, k) : 0;
+  return own > large ? own : large;
+}
+
+// The 192x256-tile kernel where it takes the shape (N % 8 == 0) and its time
+// estimate is the lower (on MI355X: the 16384-row DiT shapes; 4096^3,
+// 2048x8192x2048 and the 512-row shapes stay on 128x128 tiles, which the
+// estimates rank the same way as the measurements).
+int w8a8_choose(int64_t m, int64_t n, int64_t k) {
+  if (n % 8 != 0) return 0;
+  return plan_w8a8_large(m, n, k).cost < plan_w8a8(m, n, k).cost ? 1 : 0;
 }
 
 hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const float* s,
                             uint16_t* y, int64_t m, int64_t n, int64_t k, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+                            size_t ws_bytes, hipStream_t stream, int kind) {
+  if (kind < 0) kind = w8a8_choose(m, n, k);
+  if (kind == 1) return launch_gemm_w8a8_large(xq, xs, q, s, y, m, n, k, ws, ws_bytes, stream);
   const W8a8Plan p = plan_w8a8(m, n, k);
   const int gk = (int)((k + kTile - 1) / kTile);
   const int tiles_m = (int)((m + kTile - 1) / kTile);

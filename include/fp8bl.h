@@ -211,6 +211,17 @@ int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t
                           const float* scale_inv, uint16_t* y, int64_t m, int64_t n, int64_t k,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* fp8_block_linear_w8a8 with the kernel named: FP8BL_PATH_AUTO (what
+ * fp8_block_linear_w8a8 does), FP8BL_PATH_TILED (128 x 128 tiles) or
+ * FP8BL_PATH_LARGE (256 x 256 tiles, one workgroup per compute unit; needs
+ * n % 8 == 0 and n < 2^21). Any other path, or LARGE with another n, is
+ * FP8BL_INVALID_ARG. The workspace rule is the same for every path. Both
+ * kernels meet the same bound; their outputs may differ in the last bit
+ * where their fp32 sums do. */
+int fp8_block_linear_w8a8_ex(const uint8_t* xq, const float* x_scale, const uint8_t* q,
+                             const float* scale_inv, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                             void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
 /* The whole W8A8 route from a bf16 activation: fp8_act_quantize into the
  * workspace, then fp8_block_linear_w8a8. Same result as those two calls.
  *   x          [m,k] bf16 bits, finite (in, 16-B aligned)

@@ -130,6 +130,8 @@ int main() {
         const int b = fp8_block_linear_w8a8(q, s, at<uint8_t>(40 * F), at<float>(48 * F), y, m, n, k,
                                             nullptr, 0, nullptr);
         const int c = fp8_block_linear_w8a8_bf16(x, q, s, y, m, n, k, nullptr, 0, nullptr);
+        const int c2 = fp8_block_linear_w8a8_ex(q, s, at<uint8_t>(40 * F), at<float>(48 * F), y, m, n, k,
+                                                nullptr, 0, FP8BL_PATH_LARGE, nullptr);
         const int d = fp8_block_mlp_gate_up_ex(x, q, s, at<uint8_t>(40 * F), at<float>(48 * F), y, m, n, k,
                                                FP8BL_PATH_LARGE, nullptr);
         const int e = fp8_block_mlp_gate_up_ex(x, q, s, at<uint8_t>(40 * F), at<float>(48 * F), y, m, n, k,
@@ -138,7 +140,7 @@ int main() {
           std::printf("FAIL gated path 7 accepted\n");
           ++g_fail;
         }
-        for (int st : {a, b, c, d})
+        for (int st : {a, b, c, c2, d})
           if (st == FP8BL_OK && m != 0 && n != 0) {
             std::printf("FAIL gated/w8a8 accepted m=%lld n=%lld k=%lld\n", (long long)m, (long long)n,
                         (long long)k);

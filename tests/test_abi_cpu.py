@@ -21,7 +21,7 @@ def test_header_symbols_exported(lib):
         "fp8_block_dequant", "fp8_block_linear_workspace_size", "fp8_block_linear",
         "fp8_block_linear_ex", "fp8_block_quantize", "fp8_block_quantize_bf16",
         "fp8_block_mlp_gate_up", "fp8_block_mlp_gate_up_ex", "fp8_act_quantize", "fp8_block_linear_w8a8_workspace_size",
-        "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_bf16", "fp8_block_stream_read",
+        "fp8_block_linear_w8a8", "fp8_block_linear_w8a8_ex", "fp8_block_linear_w8a8_bf16", "fp8_block_stream_read",
         "fp8_block_linear_noalloc",
     }
     for name in names:
@@ -253,3 +253,18 @@ def test_element_count_limit_is_strict(lib):
 ])
 def test_stream_read_argument_errors(lib, args, status):
     assert L.stream_read_raw(*args) == status
+
+
+@pytest.mark.parametrize("n,path,status", [
+    (8, 2, L.FP8BL_INVALID_ARG),          # SKINNY is not a W8A8 kernel
+    (8, 4, L.FP8BL_INVALID_ARG),
+    (12, L.PATH_LARGE, L.FP8BL_INVALID_ARG),   # the 192x256-tile kernel needs N % 8 == 0
+    (1 << 21, L.PATH_LARGE, L.FP8BL_INVALID_ARG),
+    (12, L.PATH_TILED, L.FP8BL_OK),
+    (16, L.PATH_LARGE, L.FP8BL_OK),
+])
+def test_w8a8_ex_paths(lib, n, path, status):
+    """Path checks of the kernel-choosing W8A8 call come before any device
+    work (M = 0: a valid call returns at once)."""
+    assert L.linear_w8a8_ex_raw(FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 0, n, 16, 0, 0,
+                                path) == status

@@ -30,10 +30,15 @@ def gpu_act_quantize(x_bits):
     return u8(xq), f32(xs)
 
 
-def run_w8a8(xq, xs, q, s):
-    y = F.fp8_block_linear_w8a8(to_u8(xq), to_f32(xs), to_u8(q), to_f32(s))
+def run_w8a8(xq, xs, q, s, path=F.PATH_AUTO):
+    y = F.fp8_block_linear_w8a8(to_u8(xq), to_f32(xs), to_u8(q), to_f32(s), path=path)
     torch.cuda.synchronize()
     return bits(y)
+
+
+# the kernels a shape can be forced onto (the 256-row-tile kernel needs N % 8 == 0)
+def _paths(n):
+    return [F.PATH_TILED, F.PATH_LARGE] if n % 8 == 0 else [F.PATH_TILED]
 
 
 def assert_bound(y_bits, y_ref, a_ref, label):
@@ -109,10 +114,34 @@ def _w8a8_inputs(seed, m, n, k):
 ])
 def test_w8a8_small_shapes(m, n, k):
     xq, xs, q, s = _w8a8_inputs(m * 13 + n * 7 + k, m, n, k)
-    say("w8a8", m, n, k)
-    y = run_w8a8(xq, xs, q, s)
     yr, ar = O.linear_w8a8_exact(xq, xs, q, s)
-    assert_bound(y, yr, ar, f"w8a8 {m}x{n}x{k}")
+    for path in [F.PATH_AUTO] + _paths(n):
+        say("w8a8", m, n, k, "path", path)
+        y = run_w8a8(xq, xs, q, s, path)
+        assert_bound(y, yr, ar, f"w8a8 {m}x{n}x{k} path {path}")
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (193, 264, 400),       # one row past a 192-row tile, the last wave past N, K % 128 = 16
+    (2000, 8192, 256),     # 11 x 32 = 352 tiles: several units per workgroup's walk
+    (700, 1544, 3088),     # many K blocks, the last partial; N % 256 = 8
+    (512, 5120, 5120),     # split K
+])
+def test_w8a8_large_kernel_shapes(m, n, k):
+    """The 192 x 256-tile kernel forced, compared in full."""
+    xq, xs, q, s = _w8a8_inputs(m * 11 + n + k, m, n, k)
+    say("w8a8 large", m, n, k)
+    y = run_w8a8(xq, xs, q, s, F.PATH_LARGE)
+    yr, ar = O.linear_w8a8_exact(xq, xs, q, s)
+    assert_bound(y, yr, ar, f"w8a8 large {m}x{n}x{k}")
+
+
+def test_w8a8_large_path_rejects_ragged_n():
+    xq, xs, q, s = _w8a8_inputs(37, 64, 132, 128)
+    with pytest.raises(F.Fp8blError):
+        run_w8a8(xq, xs, q, s, F.PATH_LARGE)
+    with pytest.raises(F.Fp8blError):
+        run_w8a8(xq, xs, q, s, F.PATH_SKINNY)
 
 
 def test_w8a8_all_codes_pow2_scales():
@@ -125,10 +154,11 @@ def test_w8a8_all_codes_pow2_scales():
     q = np.resize(finite[::-1], n * k).reshape(n, k).copy()
     xs = (2.0 ** rng.integers(-10, 4, (4, m))).astype(np.float32)
     s = (2.0 ** rng.integers(-12, -2, (2, 4))).astype(np.float32)
-    say("w8a8 all codes")
-    y = run_w8a8(xq, xs, q, s)
     yr, ar = O.linear_w8a8_exact(xq, xs, q, s)
-    assert_bound(y, yr, ar, "w8a8 all codes")
+    for path in _paths(n):
+        say("w8a8 all codes, path", path)
+        y = run_w8a8(xq, xs, q, s, path)
+        assert_bound(y, yr, ar, f"w8a8 all codes path {path}")
 
 
 def test_w8a8_one_hot_exact():
@@ -141,18 +171,20 @@ def test_w8a8_one_hot_exact():
     xs = np.ones((3, m), np.float32)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     q, s = O.quantize(w)
-    say("w8a8 one-hot")
-    y = run_w8a8(xq, xs, q, s)
     yr, _ = O.linear_w8a8_exact(xq, xs, q, s)
     # y = bf16(fl32(e4m3(q) * s)) exactly: one product, one rounding
     exp = O.bf16_rne_bits(yr.astype(np.float32))
-    assert np.array_equal(y, exp)
+    for path in _paths(n):
+        say("w8a8 one-hot, path", path)
+        y = run_w8a8(xq, xs, q, s, path)
+        assert np.array_equal(y, exp)
 
 
 def test_w8a8_zero_and_empty():
     xq, xs, q, s = _w8a8_inputs(35, 64, 256, 512)
-    y = run_w8a8(np.zeros_like(xq), xs, q, s)
-    assert np.all((y & 0x7FFF) == 0)
+    for path in _paths(256):
+        y = run_w8a8(np.zeros_like(xq), xs, q, s, path)
+        assert np.all((y & 0x7FFF) == 0)
     y = F.fp8_block_linear_w8a8(to_u8(xq[:0]), to_f32(xs[:, :0]), to_u8(q), to_f32(s))
     torch.cuda.synchronize()
     assert tuple(y.shape) == (0, 256)
