@@ -363,10 +363,10 @@ def measure(args, workload, op="linear", path="auto", steps=None, warmup=None):
             F.fp8_block_linear_w8a8_bf16(x, q, s, out=y, workspace=ws)
         elif op == "w8a8_gemm":
             xq, xs = xqs[i % rotate]
-            F.fp8_block_linear_w8a8(xq, xs, q, s, out=y, workspace=ws)
+            F.fp8_block_linear_w8a8(xq, xs, q, s, out=y, workspace=ws, path=path_id)
         elif op == "mlp":
             qu, su = ups[i % rotate]
-            F.fp8_block_mlp_gate_up(x, q, s, qu, su, out=y)
+            F.fp8_block_mlp_gate_up(x, q, s, qu, su, out=y, path=path_id)
         elif op == "dequant":
             F.fp8_block_dequant(q, s, out=wouts[i % rotate])
         else:
@@ -467,7 +467,8 @@ def main():
                     help="the workload of the headline line (default: the M=16384 DiT MLP "
                          "up projection, 16384x12288x3072)")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS),
-                    help="kernel choice for --op linear (auto: the library's own)")
+                    help="kernel choice for --op linear, w8a8_gemm and mlp (auto: the library's "
+                         "own; w8a8_gemm and mlp take tiled or large)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the skinny-M (M=16, M=1) HBM-bound lines")

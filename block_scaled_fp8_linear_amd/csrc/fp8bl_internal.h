@@ -28,6 +28,7 @@ hipError_t launch_gemm_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q
                             uint16_t* y, int64_t m, int64_t n, int64_t k, void* ws,
                             size_t ws_bytes, hipStream_t stream, int kind = -1);
 struct W8a8LargePlan {
+  int bm;           // X rows per tile: 192 or 128
   int splits, kb_per_split;
   double cost;      // time estimate, microseconds
 };

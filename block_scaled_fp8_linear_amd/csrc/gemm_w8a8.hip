@@ -325,10 +325,11 @@ size_t w8a8_partials_bytes(int64_t m, int64_t n, int64_t k) {
   return own > large ? own : large;
 }
 
-// The 192x256-tile kernel where it takes the shape (N % 8 == 0) and its time
-// estimate is the lower (on MI355X: the 16384-row DiT shapes; 4096^3,
-// 2048x8192x2048 and the 512-row shapes stay on 128x128 tiles, which the
-// estimates rank the same way as the measurements).
+// The large-tile kernel (192 or 128 X rows x 256 weight rows) where it takes
+// the shape (N % 8 == 0) and its time estimate is the lower. Measured on
+// MI355X it is faster on the DiT shapes, 4096^3, 2048 x 8192 x 2048,
+// 1536 x 8192 x 2048 and 512 x 25600 x 5120, and level with the 128 x 128
+// kernel on 512 x 5120 x 5120; the estimates rank these the same way.
 int w8a8_choose(int64_t m, int64_t n, int64_t k) {
   if (n % 8 != 0) return 0;
   return plan_w8a8_large(m, n, k).cost < plan_w8a8(m, n, k).cost ? 1 : 0;

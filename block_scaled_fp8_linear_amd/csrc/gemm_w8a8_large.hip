@@ -53,27 +53,34 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 128;                     // K per step: one scale block
-constexpr int kBM = 192;                     // X rows per tile
-constexpr int kMB = kBM / 16;                // 16-row X blocks
 constexpr int kBN = 256;                     // weight rows per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStages = 2;
-constexpr int kXBytes = kBM * kBK;           // X codes of a stage
 constexpr int kWBytes = kBN * kBK;           // weight codes of a stage
-constexpr int kSxOff = kXBytes + kWBytes;    // 256 activation scales
-constexpr int kSwOff = kSxOff + 256 * 4;     // one 256-byte weight-scale slot per wave
-constexpr int kStageBytes = kSwOff + kWaves * 256;
-constexpr int kXLoads = kBM / kWaves / 8;    // 16-byte loads per lane per step: X rows
-constexpr int kWLoads = kBN / kWaves / 8;    //   and weight rows (8 rows of 128 B each)
+constexpr int kWLoads = kBN / kWaves / 8;    // 16-byte loads per lane per step: weight rows (8 of 128 B each)
 constexpr uint32_t kOob = 0x80000000u;
 constexpr int kFmtE4M3 = 0;                  // f8f6f4 operand format code of E4M3
 constexpr int kE8M0One = 127;                // E8M0 exponent of 1.0
 
-static_assert(kStageBytes % 256 == 0, "stages keep the LDS bank phase of their rows");
-static_assert(kStages * kStageBytes <= 160 * 1024, "two stages fit the CU's LDS");
-static_assert(kXLoads == 6 && kWLoads == 8, "a wave's loads cover its 48 X and 64 weight rows");
-static_assert(((kBM / kWaves) & 15) == 0, "a wave's X rows start at a multiple of 16 (swizzle phase)");
+// Stage layout for a tile of BM X rows (192 or 128): X codes, weight codes,
+// 256 activation-scale slots, one 256-byte weight-scale slot per wave; as
+// many stages (two or three) as fit the CU's 160 KB of LDS. Loads run
+// kStages - 1 steps ahead.
+template <int BM>
+struct Stage {
+  static constexpr int kMB = BM / 16;                  // 16-row X blocks
+  static constexpr int kXBytes = BM * kBK;
+  static constexpr int kSxOff = kXBytes + kWBytes;
+  static constexpr int kSwOff = kSxOff + 256 * 4;
+  static constexpr int kBytes = kSwOff + kWaves * 256;
+  static constexpr int kXLoads = BM / kWaves / 8;      // X row loads per lane per step
+  static constexpr int kLoads = kXLoads + kWLoads + 2; // loads per wave and step
+  static constexpr int kStages = 3 * kBytes <= 160 * 1024 ? 3 : 2;
+  static_assert(kBytes % 256 == 0, "stages keep the LDS bank phase of their rows");
+  static_assert(kStages * kBytes <= 160 * 1024, "the stages fit the CU's LDS");
+  static_assert(((BM / kWaves) & 15) == 0, "a wave's X rows start at a multiple of 16 (swizzle phase)");
+  static_assert(kMB % 4 == 0 && kXLoads <= kWLoads, "row blocks in fours; X loads fit the load regions");
+};
 
 constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kLgkmWait0 = 0xC07F;
@@ -90,13 +97,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Physical 16-byte chunk of logical chunk c in tile row r (128-byte rows).
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
-template <bool SPLIT>
+template <int BM, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1)
 void gemm_w8a8_large_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                             const uint8_t* __restrict__ q, const float* __restrict__ s,
                             uint16_t* __restrict__ y, float* __restrict__ part, int M, int N,
                             int K, int gk, int tiles_m, int tiles_n, int kb_per_split, int splits,
                             int steps_per_unit) {
+  using St = Stage<BM>;
+  constexpr int kBM = BM, kMB = St::kMB, kXBytes = St::kXBytes, kSxOff = St::kSxOff,
+                kSwOff = St::kSwOff, kStageBytes = St::kBytes, kXLoads = St::kXLoads,
+                kStages = St::kStages, kAhead = kStages - 1;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -224,22 +235,26 @@ void gemm_w8a8_large_kernel(const uint8_t* __restrict__ xq, const float* __restr
     asm volatile("" ::: "memory");
   };
 
-  // Prologue: the first unit's first step.
+  // Prologue: the first unit's first kAhead steps (every unit has at least
+  // that many; a padded step reads zeros); wait for the first.
 #pragma unroll
-  for (int r = 0; r < kWLoads; ++r) issue_region(0, 0, r);
-  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  for (int a = 0; a < kAhead; ++a)
+#pragma unroll
+    for (int r = 0; r < kWLoads; ++r) issue_region(a * kStageBytes, a, r);
+  __builtin_amdgcn_s_waitcnt(vm_wait((kAhead - 1) * St::kLoads));
   wg_barrier();
 
-  int S = 0;
-  int lkt = 0;               // step (of LU) most recently loaded
+  int S = 0;                 // stage of the step being computed
+  int lkt = kAhead - 1;      // step (of LU) most recently loaded
   for (int ci = 0; ci < my_units; ++ci) {
     for (int kt = 0; kt < steps_per_unit; ++kt) {
-      // the next step: of LU, or step 0 of the next unit
+      // the step kAhead ahead: of LU, or an early step of the next unit
       if (++lkt == steps_per_unit) {
         set_load_unit(unit_of(ci + 1));
         lkt = 0;
       }
-      const int sb = S * kStageBytes, sbn = (S ^ 1) * kStageBytes;
+      const int sb = S * kStageBytes;
+      const int sbn = (S + kAhead < kStages ? S + kAhead : S + kAhead - kStages) * kStageBytes;
 
       i32x8 wf[4];
 #pragma unroll
@@ -258,7 +273,14 @@ void gemm_w8a8_large_kernel(const uint8_t* __restrict__ xq, const float* __restr
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         if (mb + 2 < kMB) xf[(mb + 2) % 3] = read_x(sb, mb + 2);
-        if (mb < kWLoads) issue_region(sbn, lkt, mb);
+        if constexpr (kMB > kWLoads) {
+          if (mb < kWLoads) issue_region(sbn, lkt, mb);
+        } else if (mb < kWLoads / 2) {
+          // as many regions as loads: two per region over the first half, so
+          // the last ones are not issued just before the step's wait
+          issue_region(sbn, lkt, 2 * mb);
+          issue_region(sbn, lkt, 2 * mb + 1);
+        }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           pr[mb & 1][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -296,25 +318,26 @@ void gemm_w8a8_large_kernel(const uint8_t* __restrict__ xq, const float* __restr
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           acc[nb][kMB - 1][r] = __builtin_fmaf(pr[(kMB - 1) & 1][nb][r], sc[(kMB - 1) & 1], acc[nb][kMB - 1][r]);
-      // this wave's part of the next stage has landed and its reads of this
-      // stage have returned; after the barrier every wave's have
-      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+      // this wave's part of the next stage has landed (only this step's own
+      // loads may still be in flight) and its reads of this stage have
+      // returned; after the barrier every wave's have
+      __builtin_amdgcn_s_waitcnt(vm_wait((kAhead - 1) * St::kLoads));
       __builtin_amdgcn_s_waitcnt(kLgkmWait0);
       wg_barrier();
-      S ^= 1;
+      S = S + 1 == kStages ? 0 : S + 1;
     }
 
-    // ---- Epilogue of unit ci (the next unit's first step is loaded, in
-    // stage S). acc[nb][mb][r] is output row m0 + 16mb + l % 16, column
-    // n0 + 64w + 16nb + 4(l / 16) + r. The wave's 64 weight rows (8 KB) of
-    // the stage the last step used (S ^ 1) are its own: every wave finished
+    // ---- Epilogue of unit ci (the next unit's first steps are loaded or in
+    // flight, from stage S on). acc[nb][mb][r] is output row m0 + 16mb +
+    // l % 16, column n0 + 64w + 16nb + 4(l / 16) + r. The wave's 64 weight
+    // rows (8 KB) of the stage the last step used are its own: every wave finished
     // reading that stage before the last barrier, and only this wave refills
     // those rows, with loads it issues after these reads have returned. Each
     // 16-row block goes there row-major and comes back as whole 128-byte
     // (bf16) or 256-byte (fp32) rows, 16 bytes per lane.
     const Unit CU = unit_of(ci);
     const int rows = min(M - CU.m0, kBM);
-    const int tb = (S ^ 1) * kStageBytes + kXBytes + (kBN / kWaves) * wave * kBK;
+    const int tb = (S == 0 ? kStages - 1 : S - 1) * kStageBytes + kXBytes + (kBN / kWaves) * wave * kBK;
     int le;
     asm volatile("" : "=v"(le) : "0"(lane));   // keeps the addresses below out of the main loop's registers
     const int er = le & 15, eg = le >> 4;
@@ -408,30 +431,39 @@ int device_cus() {
 
 }  // namespace
 
-// Split count and time estimate (microseconds): the busiest CU runs
-// ceil(units / 256) units of `steps` 192x256x128 steps each, plus about 4 us
-// per unit (its first loads and its epilogue); K splits add the fp32
-// partials' round trip.
+// Tile height, split count and time estimate (microseconds): the busiest
+// CU runs ceil(units / 256) units of `steps` steps each, plus about 4 us per
+// unit (its first loads and its epilogue); K splits add the fp32 partials'
+// round trip. Per 256-wide weight slab and 128-wide K block, a step of 192 X
+// rows takes 1.45 us on a CU and one of 128 rows 1.16 us (measured on
+// 16384 x 3072 x 3072, 4096^3 and 512 x 25600 x 5120; the smaller tile
+// issues 14 loads per wave for 32 MFMAs against 16 for 48). The lower tile
+// wins where it fills the last round better: 16384 x 3072 x 3072 187 against
+// 201 us (1536 tiles of 128 rows, 6 full rounds, against 1032 of 192 rows,
+// 4.03 rounds), 4096^3 83 against 103; 192 rows win at 16384 x 12288 x 3072
+// (630 against 771) and 1536 x 8192 x 2048 (35 against 45). The estimates
+// rank all eight shapes measured the same way.
 W8a8LargePlan plan_w8a8_large(int64_t m, int64_t n, int64_t k) {
-  constexpr double kStepUs = 1.45;     // one 192x256x128 step on one CU (measured at 16384 rows)
   const int gk = (int)((k + kBK - 1) / kBK);
-  const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
-  W8a8LargePlan p{1, gk, 0.0};
-  double best = 1e300;
-  for (int sp = 1; sp <= 8; ++sp) {
-    const int steps = (gk + sp - 1) / sp;
-    if (sp > 1 && steps < 4) break;
-    const int64_t per_cu = (tiles * sp + 255) / 256;
-    double cost = (double)per_cu * (steps * kStepUs + 4.0);
-    if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
-    if (cost < best) {
-      best = cost;
-      p.splits = sp;
+  W8a8LargePlan p{192, 1, gk, 1e300};
+  for (const int bm : {192, 128}) {
+    const double step_us = bm == 192 ? 1.45 : 1.16;
+    const int64_t tiles = ((m + bm - 1) / bm) * ((n + kBN - 1) / kBN);
+    for (int sp = 1; sp <= 8; ++sp) {
+      const int steps = (gk + sp - 1) / sp;
+      if (sp > 1 && steps < 4) break;
+      const int64_t per_cu = (tiles * sp + 255) / 256;
+      double cost = (double)per_cu * (steps * step_us + 4.0);
+      if (sp > 1) cost += (double)(6 * sp + 2) * (double)(m * n) / 5.0e6;
+      if (cost < p.cost) {
+        p.cost = cost;
+        p.bm = bm;
+        p.splits = sp;
+      }
     }
   }
   p.kb_per_split = (gk + p.splits - 1) / p.splits;
   p.splits = (gk + p.kb_per_split - 1) / p.kb_per_split;
-  p.cost = best;
   return p;
 }
 
@@ -441,30 +473,44 @@ size_t w8a8_large_partials_bytes(int64_t m, int64_t n, int64_t k) {
   return round_up((size_t)p.splits * partial_slab(m, n) * sizeof(float), kWorkspaceAlign);
 }
 
+namespace {
+
+template <int BM>
+hipError_t launch_bm(const uint8_t* xq, const float* xs, const uint8_t* q, const float* s,
+                     uint16_t* y, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
+                     const W8a8LargePlan& p, hipStream_t stream) {
+  const int gk = (int)((k + kBK - 1) / kBK);
+  const int tiles_m = (int)((m + BM - 1) / BM);
+  const int tiles_n = (int)((n + kBN - 1) / kBN);
+  const int units = tiles_m * tiles_n * p.splits;
+  const int grid = units < device_cus() ? units : device_cus();
+  // every unit runs at least the prologue's kStages - 1 steps (padded ones read zeros)
+  const int spu = p.kb_per_split > Stage<BM>::kStages - 1 ? p.kb_per_split : Stage<BM>::kStages - 1;
+  if (p.splits == 1) {
+    hipLaunchKernelGGL((gemm_w8a8_large_kernel<BM, false>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                       stream, xq, xs, q, s, y, nullptr, (int)m, (int)n, (int)k, gk, tiles_m,
+                       tiles_n, p.kb_per_split, 1, spu);
+    return hipGetLastError();
+  }
+  if (ws == nullptr || ws_bytes < w8a8_large_partials_bytes(m, n, k)) return hipErrorInvalidValue;
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL((gemm_w8a8_large_kernel<BM, true>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                     stream, xq, xs, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
+                     p.kb_per_split, p.splits, spu);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce_partials(part, y, p.splits, m, n, stream);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_w8a8_large(const uint8_t* xq, const float* xs, const uint8_t* q,
                                   const float* s, uint16_t* y, int64_t m, int64_t n, int64_t k,
                                   void* ws, size_t ws_bytes, hipStream_t stream) {
   if ((n & 7) != 0) return hipErrorInvalidValue;
   const W8a8LargePlan p = plan_w8a8_large(m, n, k);
-  const int gk = (int)((k + kBK - 1) / kBK);
-  const int tiles_m = (int)((m + kBM - 1) / kBM);
-  const int tiles_n = (int)((n + kBN - 1) / kBN);
-  const int units = tiles_m * tiles_n * p.splits;
-  const int grid = units < device_cus() ? units : device_cus();
-  if (p.splits == 1) {
-    hipLaunchKernelGGL(gemm_w8a8_large_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0,
-                       stream, xq, xs, q, s, y, nullptr, (int)m, (int)n, (int)k, gk, tiles_m,
-                       tiles_n, p.kb_per_split, 1, p.kb_per_split);
-    return hipGetLastError();
-  }
-  if (ws == nullptr || ws_bytes < w8a8_large_partials_bytes(m, n, k)) return hipErrorInvalidValue;
-  float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL(gemm_w8a8_large_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                     xq, xs, q, s, y, part, (int)m, (int)n, (int)k, gk, tiles_m, tiles_n,
-                     p.kb_per_split, p.splits, p.kb_per_split);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_reduce_partials(part, y, p.splits, m, n, stream);
+  return p.bm == 192 ? launch_bm<192>(xq, xs, q, s, y, m, n, k, ws, ws_bytes, p, stream)
+                     : launch_bm<128>(xq, xs, q, s, y, m, n, k, ws, ws_bytes, p, stream);
 }
 
 }  // namespace fp8bl

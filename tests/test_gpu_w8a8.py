@@ -122,13 +122,15 @@ def test_w8a8_small_shapes(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [
-    (193, 264, 400),       # one row past a 192-row tile, the last wave past N, K % 128 = 16
-    (2000, 8192, 256),     # 11 x 32 = 352 tiles: several units per workgroup's walk
-    (700, 1544, 3088),     # many K blocks, the last partial; N % 256 = 8
+    (193, 264, 400),       # one row past a tile, the last wave past N, K % 128 = 16
+    (2000, 8192, 256),     # 16 x 32 = 512 tiles: several units per workgroup's walk
+    (700, 1544, 3088),     # many K blocks, the last partial; N % 256 = 8; split K
     (512, 5120, 5120),     # split K
+    (1500, 8184, 400),     # 192-row tiles (256 of them fill one round), ragged rows and N
 ])
 def test_w8a8_large_kernel_shapes(m, n, k):
-    """The 192 x 256-tile kernel forced, compared in full."""
+    """The large-tile kernel forced (its planner picks 128 or 192 X rows per
+    tile; the last shape takes 192), compared in full."""
     xq, xs, q, s = _w8a8_inputs(m * 11 + n + k, m, n, k)
     say("w8a8 large", m, n, k)
     y = run_w8a8(xq, xs, q, s, F.PATH_LARGE)
