@@ -90,6 +90,13 @@ size_t x_scale_elems(int64_t m, int64_t k) {
   return (size_t)((k + FP8BL_BLOCK - 1) / FP8BL_BLOCK) * (size_t)m;
 }
 
+// The W8A8 GEMMs address the activation scales through a 32-bit buffer
+// range: at most 2^32 - 4 bytes of them (reached only with very small K and
+// M near 2^31).
+bool x_scale_fits(int64_t m, int64_t k) {
+  return m <= 0 || k <= 0 || x_scale_elems(m, k) * 4 < ((size_t)1 << 32);
+}
+
 // Shape rules of the W8A8 GEMM (as the bf16 linear) plus the operands'
 // alignment and the output's overlap with them.
 int validate_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const float* s,
@@ -100,6 +107,7 @@ int validate_w8a8(const uint8_t* xq, const float* xs, const uint8_t* q, const fl
   if (k > kMaxLinearK) return FP8BL_INVALID_ARG;
   if (m > 0 && m * k >= kMaxElems) return FP8BL_INVALID_ARG;
   if (m > 0 && n > 0 && m * n >= kMaxElems) return FP8BL_INVALID_ARG;
+  if (!x_scale_fits(m, k)) return FP8BL_INVALID_ARG;
   if (m == 0 || n == 0) return FP8BL_OK;
   if (!xq || !xs || !q || !s || !y) return FP8BL_INVALID_ARG;
   if (!aligned(xq, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(xs, 4) || !aligned(s, 4))
@@ -387,6 +395,7 @@ FP8BL_EXPORT int fp8_block_linear_w8a8_bf16(const uint16_t* x, const uint8_t* q,
                                             size_t workspace_bytes, hipStream_t stream) {
   int st = validate_linear(x, q, scale_inv, y, m, n, k, FP8BL_PATH_AUTO);
   if (st != FP8BL_OK) return st;
+  if (!x_scale_fits(m, k)) return FP8BL_INVALID_ARG;
   if (m == 0 || n == 0) return FP8BL_OK;
   const size_t need = fp8_block_linear_w8a8_workspace_size(m, n, k);
   if (workspace == nullptr || workspace_bytes < need) return FP8BL_WORKSPACE;

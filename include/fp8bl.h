@@ -206,7 +206,9 @@ size_t fp8_block_linear_w8a8_workspace_size(int64_t m, int64_t n, int64_t k);
  *   workspace    as for fp8_block_linear (fp32 split-K partials), at least
  *                fp8_block_linear_w8a8_workspace_size bytes or NULL when the
  *                shape needs none; calls sharing it must be ordered.
- * K may be at most 2^20. */
+ * K may be at most 2^20, and the activation scales (4 * m * ceil(k/128)
+ * bytes) must stay below 2^32 bytes (FP8BL_INVALID_ARG otherwise; reached
+ * only with very small k and m near 2^31). */
 int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t* q,
                           const float* scale_inv, uint16_t* y, int64_t m, int64_t n, int64_t k,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);

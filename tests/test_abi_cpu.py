@@ -268,3 +268,15 @@ def test_w8a8_ex_paths(lib, n, path, status):
     work (M = 0: a valid call returns at once)."""
     assert L.linear_w8a8_ex_raw(FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, 0, n, 16, 0, 0,
                                 path) == status
+
+
+def test_w8a8_activation_scales_over_4gib_rejected(lib):
+    """The W8A8 GEMMs address the activation scales with 32-bit buffer
+    offsets: 4 * m * ceil(k/128) bytes must stay below 2^32. With k = 16 that
+    is m < 2^30, a shape the other limits (m*k, m*n < 2^35) still allow."""
+    m, n, k = 1 << 30, 8, 16
+    for path in (L.PATH_AUTO, L.PATH_TILED, L.PATH_LARGE):
+        assert L.linear_w8a8_ex_raw(FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, m, n, k, 0, 0,
+                                    path) == L.FP8BL_INVALID_ARG
+    assert L.linear_w8a8_bf16_raw(FAKE, 3 * FAKE, 4 * FAKE, 8 * FAKE, m, n, k, 0, 0) == \
+        L.FP8BL_INVALID_ARG
