@@ -5,30 +5,32 @@
 // "Changes": the converter's 128x128 weight blocks and the Blackwell route's
 // per-token activation quantizer feeding a groupwise GEMM).
 //
-// Tile 192 (X rows) x 256 (weight rows), one workgroup of four waves per CU,
-// persistent over (tile, K split) units like the bf16 large-M kernel. Wave w
-// owns weight rows [64w, 64w + 64) of the tile against all 192 X rows: 4 x 12
-// blocks of v_mfma_scale_f32_16x16x128_f8f6f4 (E8M0 block scales held at
-// 1.0: the scales here are arbitrary fp32), 192 fp32 accumulators per lane.
-// (With 256 X rows the accumulators take all 256 VGPRs a lane can address,
-// every block sum lands in AGPRs and has to be copied out before its FMA:
-// twice the VALU work, more than the MFMA time.)
+// Tile BM (X rows: 192 or 128, picked per shape) x 256 (weight rows), one
+// workgroup of four waves per CU, persistent over (tile, K split) units like
+// the bf16 large-M kernel. Wave w owns weight rows [64w, 64w + 64) of the
+// tile against all BM X rows: 4 x (BM / 16) blocks of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E8M0 block scales held at 1.0: the
+// scales here are arbitrary fp32), BM fp32 accumulators per lane. (With 256
+// X rows the accumulators take all 256 VGPRs a lane can address, every block
+// sum lands in AGPRs and has to be copied out before its FMA: twice the VALU
+// work, more than the MFMA time.)
 // The weight block is the A operand and X the B operand, so a lane's four
 // results of a block are four consecutive output columns of one output row:
 // the block's combined scale is one number per lane (its X row's scale times
 // the wave's weight scale, the wave's 64 rows lying in one 128-row block).
-// Per K block a wave reads 12 X fragments from LDS, each feeding 4 MFMAs,
-// half the LDS bytes per MFMA of the 64 x 64 per-wave tile.
+// Per K block a wave reads BM / 16 X fragments from LDS, each feeding 4
+// MFMAs, half the LDS bytes per MFMA of the 64 x 64 per-wave tile.
 //
-// One step = one 128-wide K block. Two LDS stages of 58 KB each: X codes
-// (192 rows x 128 B), weight codes (256 rows x 128 B), the tile's 192
-// activation scales and one weight scale per wave, all moved global -> LDS
-// by direct-to-LDS buffer loads (no registers), the 16-byte chunks of a row
-// XOR-permuted by (row & 7) ^ ((row >> 3) & 1) so the operand reads (16 lanes
-// on 16 consecutive rows, one chunk) are conflict-free. A wave loads only its
-// own 48 X rows and 64 weight rows, 16 loads per step, spread over the first
-// two thirds of the step for the next step; the barrier at the end of each
-// step hands the stages over.
+// One step = one 128-wide K block. A stage holds the step's X codes (BM rows
+// x 128 B), weight codes (256 rows x 128 B), the tile's activation scales and
+// one weight scale per wave (58 KB at 192 rows, 50 KB at 128), all moved
+// global -> LDS by direct-to-LDS buffer loads (no registers), the 16-byte
+// chunks of a row XOR-permuted by (row & 7) ^ ((row >> 3) & 1) so the operand
+// reads (16 lanes on 16 consecutive rows, one chunk) are conflict-free. Three
+// stages fit at 128 rows (loads two steps ahead), two at 192 (one step ahead).
+// A wave loads only its own BM / 4 X rows and 64 weight rows (16 or 14 loads
+// per step), spread over the first part of the step; the barrier at the end
+// of each step hands the stages over.
 //
 // MFMA operand layout (16x16x128, 8-bit operands): lane l supplies the 32
 // codes of row l % 16 of its block at K quarter l / 16 (chunks 2(l/16) and
