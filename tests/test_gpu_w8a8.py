@@ -127,10 +127,11 @@ def test_w8a8_small_shapes(m, n, k):
     (700, 1544, 3088),     # many K blocks, the last partial; N % 256 = 8; split K
     (512, 5120, 5120),     # split K
     (1500, 8184, 400),     # 192-row tiles (256 of them fill one round), ragged rows and N
+    (190, 12280, 4000),    # 192-row tiles with a 4-way K split, ragged rows, N and K
 ])
 def test_w8a8_large_kernel_shapes(m, n, k):
     """The large-tile kernel forced (its planner picks 128 or 192 X rows per
-    tile; the last shape takes 192), compared in full."""
+    tile; the last two shapes take 192), compared in full."""
     xq, xs, q, s = _w8a8_inputs(m * 11 + n + k, m, n, k)
     say("w8a8 large", m, n, k)
     y = run_w8a8(xq, xs, q, s, F.PATH_LARGE)
