@@ -289,8 +289,10 @@ def test_linear_square_tile_shapes(m, n, k):
 def test_linear_large_tile_shapes(m, n, k):
     """The 256x256 four-wave kernel forced on shapes with partial tiles in M
     and N, K tails inside a 64-wide step and a 16-wide sub-step, N % 4 != 0
-    (element stores), 8 and 4 K splits (100x700x5200, 257x1000x2576) and
-    more tiles than CUs. Full compare against the oracle."""
+    (element stores) and 8 and 4 K splits (100x700x5200, 257x1000x2576).
+    Full compare against the oracle. (Workgroups walking several units are
+    compared in full on the DiT shapes, 768 and 3072 tiles, in
+    test_gpu_fullsize.py.)"""
     x, w = random_problem(m * 3 + n * 11 + k, m, n, k)
     q, s = O.quantize(w)
     say("linear large tile", m, n, k)
