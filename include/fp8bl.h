@@ -150,8 +150,12 @@ int fp8_block_linear_noalloc(const uint16_t* x, const uint8_t* q, const float* s
  *   g = bf16_rne(x Wg_hat^T),  u = bf16_rne(x Wu_hat^T)   (as fp8_block_linear)
  *   h = bf16_rne( bf16_rne(fl32(silu(g))) * u ),  silu(g) = g / (1 + e^-g)
  * Both weights share the shape [n,k] and the input x; g and u never reach
- * memory. silu is evaluated in fp32 (a few ulp), so h is graded against the
- * exact silu(G*) U* with a bound, not bit for bit.
+ * memory. silu is evaluated in fp32 with the hardware exp2 and reciprocal
+ * (relative error at most (|g| + 4) 2^-23; below about g = -87 the
+ * exponential overflows and silu gives -0), so h is graded against the exact
+ * silu(G*) U* with a bound, not bit for bit: it can differ from the SwiGLU
+ * of the exact-silu rounding where silu(g) lies that close to a bf16
+ * rounding boundary.
  *   x                   [m,k] bf16 bits (in, 16-B aligned)
  *   q_gate, q_up        [n,k] E4M3 bytes (in, 16-B aligned)
  *   scale_inv_gate, scale_inv_up  [ceil(n/128),ceil(k/128)] fp32 (in, 4-B aligned)
@@ -215,8 +219,9 @@ int fp8_block_linear_w8a8(const uint8_t* xq, const float* x_scale, const uint8_t
 
 /* fp8_block_linear_w8a8 with the kernel named: FP8BL_PATH_AUTO (what
  * fp8_block_linear_w8a8 does), FP8BL_PATH_TILED (128 x 128 tiles) or
- * FP8BL_PATH_LARGE (256 x 256 tiles, one workgroup per compute unit; needs
- * n % 8 == 0 and n < 2^21). Any other path, or LARGE with another n, is
+ * FP8BL_PATH_LARGE (192 or 128 X rows x 256 weight rows per tile, by its
+ * planner, one persistent workgroup per compute unit; needs n % 8 == 0 and
+ * n < 2^21). Any other path, or LARGE with another n, is
  * FP8BL_INVALID_ARG. The workspace rule is the same for every path. Both
  * kernels meet the same bound; their outputs may differ in the last bit
  * where their fp32 sums do. */
