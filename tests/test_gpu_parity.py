@@ -355,6 +355,25 @@ def test_linear_reproducible(path):
     assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
 
 
+@pytest.mark.parametrize("m,n,k", [(16, 384, 256), (1, 384, 256), (32, 1000, 16), (64, 384, 256),
+                                   (5, 300, 4112), (16, 5120, 5120)])
+def test_skinny_short_k_ranges_reproducible(m, n, k):
+    """The skinny kernel where a wave's K range is one or a few super-steps
+    (its loop ends before a whole round of ring slots), or a K split or tail
+    leaves the waves unequal shares: within the bound and the same bits on
+    every call. These are the cases where a code slot could be read before
+    its loads had landed."""
+    x, w = random_problem(m * 7 + n + k, m, n, k)
+    q, s = O.quantize(w)
+    say("skinny short k ranges", m, n, k)
+    xt, qt, st = to_bf16(x), to_u8(q), to_f32(s)
+    ys = [bits(F.fp8_block_linear(xt, qt, st, path=F.PATH_SKINNY)) for _ in range(4)]
+    for y in ys[1:]:
+        assert np.array_equal(ys[0], y)
+    yr, ar = O.linear_exact(x, O.dequant(q, s))
+    assert_bound(ys[0], yr, ar, f"skinny {m}x{n}x{k}")
+
+
 def test_linear_shared_workspace_reused():
     """Split-K shapes of several sizes through one workspace filled with
     garbage, twice: the partials need no initialisation and every result
