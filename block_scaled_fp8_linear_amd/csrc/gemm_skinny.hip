@@ -41,6 +41,7 @@ namespace fp8bl {
 namespace {
 
 constexpr int kSuper = 256;               // K per super-step (16 chunks of 16 codes per row)
+constexpr unsigned kXcds = 8;              // XCDs of an MI355X; workgroups are dealt to them in turn
 constexpr uint32_t kOob = 0x80000000u;    // buffer offset past every valid range
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -71,10 +72,11 @@ constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // does not wait behind the codes coming from HBM. On MI355X (8000 x 8192,
 // rotated weight copies, same box) against the kernel this one replaced,
 // which staged the codes through registers into LDS with one super-step in
-// flight, outputs bit-identical: 16.2 against 16.8 us at M = 16, 13.7
-// against 14.8 at M = 8, 13.0 against 13.7 at M = 1. Two slots (one
+// flight (outputs bit-identical with the same start order): 16.2 against
+// 16.8 us at M = 16, 13.7 against 14.8 at M = 8, 13.0 against 13.7 at
+// M = 1. Two slots (one
 // super-step in flight behind the one computed) are fastest: three and four
-// were 4-12% slower, so the bytes in flight per CU are not what holds the
+// were 2-14% slower, so the bytes in flight per CU are not what holds the
 // rate.
 //
 // Every super-step issues the same number of loads (steps past the range
@@ -90,6 +92,7 @@ void gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   constexpr int kSlot = NT * 16 * kSuper;         // one super-step's codes of the wave's tiles
   constexpr int kLoads = NT * 4 + MT * 8;         // code and X loads per super-step
   static_assert((D - 1) * kLoads <= 63, "outstanding loads fit the vmcnt counter");
+  static_assert(NT == 1 || NT == 2, "one or two 16-row tiles per workgroup");
   static_assert(kBlock % (16 * NT) == 0, "a workgroup's rows share one scale row");
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][D][kSlot];
 
@@ -112,9 +115,9 @@ void gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const float* const srow = s + (size_t)(n0 / kBlock) * gk;
   const bool live1 = n0 + 16 < N;    // tile 1 (NT = 2) has rows
 
-  // Code loads: instruction r of tile j brings rows
-  // 4r..4r+3, 256 bytes each; lane i lands at byte 16*i of the instruction's
-  // 1 KB of the slot and fetches logical chunk (i & 15) ^ row.
+  // Code loads: instruction r of tile j brings rows 4r..4r+3, 256 bytes
+  // each; lane i lands at byte 16*i of the instruction's 1 KB of the slot
+  // and fetches logical chunk (i & 15) ^ row.
   const int lrow4 = lane >> 4;
   const int lchk = lane & 15;
   uint32_t woff[4];       // tile 0's; tile j adds j * 16 rows
@@ -136,7 +139,15 @@ void gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int count = ss1 - ss0;
-  const int rot = count > 0 ? (int)(blockIdx.x % (unsigned)count) : 0;
+  // Every workgroup walks its K range from its own starting super-step, so
+  // that at any moment the GPU reads many K offsets at once rather than all
+  // rows at one offset (rows 8 KB apart then pile onto a few HBM channels:
+  // 30% slower at 8000 x 8192). Workgroups are dealt to the 8 XCDs in turn,
+  // so starting workgroup w at w / 8 gives the workgroups on each XCD every
+  // start; w itself gave each XCD only four (4% slower at M = 16, 1% at
+  // M = 1). The order is fixed per workgroup: results are run-to-run
+  // identical.
+  const int rot = count > 0 ? (int)((blockIdx.x / kXcds) % (unsigned)count) : 0;
   auto ss_of = [&](int i) {            // i-th super-step of the range, rotated
     if (i >= count) return ss1;        // past the end: loads read nothing
     const int r = i + rot;
